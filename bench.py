@@ -1,0 +1,220 @@
+"""Benchmark of the fused linear log-prob operator on one MI355X.
+
+One step = one pass of the whole hot path over one batch of 4096 synthetic tokens shaped
+like a Qwen3-8B LM head (H=4096, real vocabulary 151669 padded to 151936, tau=0.7, no bias,
+targets sampled from the fp64 softmax, stored under tests/golden):
+  1. llp_forward   -- layout/mask indexing, fused bf16 MFMA GEMM + online max/sum-exp/
+                      target/entropy epilogue, fixed-order cross-tile combine;
+  2. llp_merge     -- rank-ordered merge of the shard partials (here one shard);
+  3. llp_backward  -- gradient recompute G (bf16), dhidden = G W, dweight += G^T h;
+  4. llp_top_p_replay x 4 shards + llp_merge -- compact top-p replay scoring of 4096 rows of
+                      fp32 logits [4096, 151936] with <= 64 candidate ids per row.
+Inputs are resident in HBM before the timed region. The value is scored tokens/s of the
+step. Per-phase times come from HIP events recorded on the stream the kernels run on.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "scored tokens/s + MFMA util, fused linear-logp fwd(+bwd) at H=4096, V=151936"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+T, H, VR, VP, TAU = 4096, 4096, 151669, 151936, 0.7
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_kernel.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "lm_head_linear_logp_amd", "csrc", f)
+                  for f in ("llp_kernels.hip", "llp_tile.hpp")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per forward-kernel launch from the committed counter summary, or None when
+    the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(rows: int = 192) -> dict:
+    """The fp64 oracle (as it stands) on `rows` rows of the same workload: forward + backward
+    of each row, timed on this host's cores; scaled to scored tokens/s."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    base = synth.config2_base()
+    tg = np.loadtxt(os.path.join(ROOT, "tests", "golden", "config2_targets.txt"), dtype=np.int64,
+                    comments="#")
+    w64 = oracle.bf16_to_f64(synth.full_weight()[:VR])   # input conversion, not timed
+    h = base["hidden"][:rows]
+    dlogp = synth.rng(2, 70).standard_normal(rows)
+    t0 = time.perf_counter()
+    f = oracle.forward(h, w64, None, TAU, tg[:rows], None, VR)
+    oracle.backward(h, w64, None, TAU, tg[:rows], None, 0, VP, VR, f["lse"], dlogp)
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "scored tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 oracle forward+backward of {rows} of the 4096 rows "
+                      f"(H=4096, V=151669/151936), {dt:.1f} s on {threads} BLAS threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=192)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the one-GPU hot path only; runs on more than one GPU are not "
+              "part of this build (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lm_head_linear_logp_amd as llp
+    import synth
+
+    info = llp.open(0)
+    log(f"library {info['version']} route {info['route']} on {info['arch']} ({info['num_cus']} CUs)")
+
+    def d16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    log("generating inputs (W 151936x4096 bf16, h 4096x4096 bf16, top-p logits 4096x151936 fp32)")
+    base = synth.config2_base()
+    tg_np = np.loadtxt(os.path.join(ROOT, "tests", "golden", "config2_targets.txt"),
+                       dtype=np.int64, comments="#")
+    W = d16(synth.full_weight())
+    h = d16(base["hidden"])
+    tg = torch.from_numpy(tg_np).cuda()
+    dlogp = torch.from_numpy(synth.rng(2, 70).standard_normal(T).astype(np.float32)).cuda()
+    tp = synth.topp_case()
+    # Algorithmic bytes of the top-p phase: per row and shard the 64 ids (512 B), the target
+    # (8 B) and 13 B of partials; each distinct candidate's logit (4 B) once; the merge reads
+    # 4 x 9 B of partials and writes logp and lse (8 B) per row.
+    uniq = sum(np.unique(r[r >= 0]).size for r in tp["replay_ids"])
+    topp_bytes = T * 4 * (64 * 8 + 8 + 13) + 4 * uniq + T * (4 * 9 + 8)
+    logits = torch.from_numpy(tp["logits"]).cuda()
+    rids = torch.from_numpy(tp["replay_ids"]).cuda()
+    rtg = torch.from_numpy(tp["targets"]).cuda()
+    del tp
+    shards = synth.shard_ranges()
+    dW = torch.zeros((VP, H), dtype=torch.float32, device="cuda")
+    dH = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+
+    def step(record):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        if e: e[0].record(stream)
+        out = llp.forward(h, W, tg, temperature=TAU, real_vocab=VR, padded_vocab=VP)
+        if e: e[1].record(stream)
+        mg = llp.merge([out])
+        if e: e[2].record(stream)
+        llp.backward(h, W, tg, mg["lse"], dlogp, temperature=TAU, real_vocab=VR, padded_vocab=VP,
+                     dweight=dW, dhidden=dH)
+        if e: e[3].record(stream)
+        parts = [llp.top_p_replay(logits[:, off:off + n], rids, rtg, temperature=TAU, offset=off,
+                                  real_vocab=VR, padded_vocab=VP, rank=r, world=4)
+                 for r, (off, n) in enumerate(shards)]
+        llp.merge(parts, want_entropy=False)
+        if e: e[4].record(stream)
+        return e
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        events.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ph = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events])  # ms
+    total_ms = float(events[0][0].elapsed_time(events[-1][4]))
+    ms_per_step = total_ms / args.steps
+    fwd_ms, merge_ms, bwd_ms, topp_ms = (float(x) for x in ph.mean(axis=0))
+    log(f"phases (ms): forward {fwd_ms:.3f} merge {merge_ms:.3f} backward {bwd_ms:.3f} "
+        f"top-p {topp_ms:.3f}; step {ms_per_step:.3f} (host wall {1e3 * wall / args.steps:.3f})")
+
+    flop_fwd = 2.0 * T * H * VR
+    ach_fwd = flop_fwd / (fwd_ms * 1e-3) / 1e12
+    flop_bwd = 3.0 * flop_fwd
+    ach_bwd = flop_bwd / (bwd_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "scored tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-8B-shaped LM head, one shard: T=4096 scored tokens, "
+                               "H=4096, V=151669 real / 151936 padded, tau=0.7, no bias; "
+                               "forward+merge+backward, plus top-p replay of 4096 rows x 4 "
+                               "shards (K=64)",
+                   "T": T, "H": H, "real_vocab": VR, "padded_vocab": VP, "temperature": TAU},
+        "roofline": {"kernel": "k_fwd (fused GEMM + online LSE epilogue; timed with its "
+                               "layout and combine launches)",
+                     "bound": "mfma", "achieved": ach_fwd, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": ach_fwd / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic()},
+        "phases_ms": {"forward": fwd_ms, "merge": merge_ms, "backward": bwd_ms,
+                      "top_p_4shards_plus_merge": topp_ms},
+        "forward_tokens_per_s": T / (fwd_ms * 1e-3),
+        "backward_tflops": ach_bwd,
+        "forward_backward_tflops": (flop_fwd + flop_bwd) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12,
+        "top_p": {"us": topp_ms * 1e3, "algorithmic_bytes": topp_bytes,
+                  "GBps": topp_bytes / (topp_ms * 1e-3) / 1e9, "peak_GBps": PEAK_HBM_GBS},
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_rows} rows")
+        del W, h, logits, dW, dH
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,307 @@
+"""Python binding of the fused linear log-prob operator's C ABI (include/llp.h).
+
+Argument marshalling only: every step of the operator runs in the HIP library libllp.so.
+PyTorch supplies device memory (outputs, workspace) and the current HIP stream. There is no
+CPU fallback: if the library is missing or the device is not a gfx950 GPU, calls raise.
+
+Functions mirror the ABI: ``open``, ``workspace_bytes``, ``forward``, ``merge``, ``backward``,
+``top_p_replay``, ``last_error``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional, Sequence
+
+import torch
+
+from . import _capi as A
+
+__all__ = ["LLPError", "open", "workspace_bytes", "forward", "merge", "backward",
+           "top_p_replay", "last_error", "STATUS_BITS"]
+
+STATUS_BITS = {"TARGET_OUT_OF_RANGE": A.LLP_STATUS_TARGET_OUT_OF_RANGE,
+               "TARGET_NOT_FOUND": A.LLP_STATUS_TARGET_NOT_FOUND,
+               "REPLAY_ID_INVALID": A.LLP_STATUS_REPLAY_ID_INVALID,
+               "LAYOUT_INVALID": A.LLP_STATUS_LAYOUT_INVALID}
+
+
+class LLPError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {A.STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_opened = {}
+
+
+def last_error() -> str:
+    return A.load().llp_last_error().decode()
+
+
+def _check(st: int, where: str):
+    if st != A.LLP_OK:
+        raise LLPError(st, where, last_error())
+
+
+def open(device: Optional[int] = None) -> dict:
+    """Load the kernels on a gfx950 device (llp_open); returns the library identity."""
+    lib = A.load()
+    if device is None:
+        device = torch.cuda.current_device()
+    if device in _opened:
+        return _opened[device]
+    info = A.llp_info()
+    _check(lib.llp_open(int(device), C.byref(info)), "llp_open")
+    d = dict(name=info.name.decode(), version=info.version.decode(), arch=info.arch.decode(),
+             route=info.route.decode(), max_replay_ids=info.max_replay_ids,
+             num_cus=info.num_cus, device=info.device)
+    _opened[device] = d
+    return d
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, name, dtype, ndim, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if ndim >= 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must be contiguous in its last dimension")
+
+
+def _request(hidden, weight, target_ids, temperature, bias, loss_mask, cu_seqlens, offset,
+             real_vocab, padded_vocab, rank, world, want_entropy, status):
+    dev = hidden.device
+    _need(hidden, "hidden", torch.bfloat16, 2, dev)
+    _need(weight, "weight", torch.bfloat16, 2, dev)
+    _need(target_ids, "target_ids", torch.int64, 1, dev)
+    T, H = hidden.shape
+    if weight.shape[1] != H:
+        raise ValueError(f"weight is {tuple(weight.shape)}, hidden size is {H}")
+    if target_ids.shape[0] != T:
+        raise ValueError("target_ids length differs from the number of rows")
+    if padded_vocab is None:
+        padded_vocab = weight.shape[0] if world == 1 else None
+    if real_vocab is None:
+        real_vocab = padded_vocab
+    if padded_vocab is None:
+        raise ValueError("padded_vocab is required for a vocabulary shard (world > 1)")
+    req = A.llp_request()
+    req.proj.hidden = _ptr(hidden)
+    req.proj.hidden_stride = hidden.stride(0) if T > 0 else H
+    req.proj.weight = _ptr(weight)
+    req.proj.weight_stride = weight.stride(0) if weight.shape[0] > 0 else H
+    if bias is not None:
+        if bias.dtype not in (torch.bfloat16, torch.float32) or bias.dim() != 1:
+            raise TypeError("bias must be a 1-d bf16 or fp32 tensor")
+        if bias.shape[0] != weight.shape[0] or bias.device != dev or bias.stride(0) != 1:
+            raise ValueError("bias must be contiguous with one value per weight row")
+        req.proj.bias = _ptr(bias)
+        req.proj.bias_dtype = A.LLP_DTYPE_F32 if bias.dtype == torch.float32 else A.LLP_DTYPE_BF16
+    req.proj.hidden_size = H
+    req.vocab.offset = int(offset)
+    req.vocab.local_size = int(weight.shape[0])
+    req.vocab.real_vocab = int(real_vocab)
+    req.vocab.padded_vocab = int(padded_vocab)
+    req.vocab.rank = int(rank)
+    req.vocab.world = int(world)
+    req.layout.num_tokens = T
+    if loss_mask is not None:
+        _need(loss_mask, "loss_mask", torch.uint8, 1, dev)
+        if loss_mask.shape[0] != T:
+            raise ValueError("loss_mask length differs from the number of rows")
+        req.layout.loss_mask = _ptr(loss_mask)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+        req.layout.cu_seqlens = _ptr(cu_seqlens)
+        req.layout.num_seqs = cu_seqlens.shape[0] - 1
+    req.target_ids = _ptr(target_ids)
+    req.temperature = float(temperature)
+    req.flags = A.LLP_FLAG_WANT_ENTROPY if want_entropy else 0
+    if status is not None:
+        _need(status, "status", torch.int32, 1, dev)
+        req.status_word = _ptr(status)
+    return req
+
+
+def workspace_bytes(req: "A.llp_request", op: int) -> int:
+    n = C.c_size_t(0)
+    _check(A.load().llp_workspace_bytes(C.byref(req), op, C.byref(n)), "llp_workspace_bytes")
+    return int(n.value)
+
+
+def _workspace(req, op, dev, workspace):
+    need = workspace_bytes(req, op)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    return workspace
+
+
+def forward(hidden: torch.Tensor, weight: torch.Tensor, target_ids: torch.Tensor, *,
+            temperature: float, bias: Optional[torch.Tensor] = None,
+            loss_mask: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+            offset: int = 0, real_vocab: Optional[int] = None,
+            padded_vocab: Optional[int] = None, rank: int = 0, world: int = 1,
+            want_entropy: bool = True, status: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
+    """llp_forward on one shard. Returns target_logit, in_range, lse, entropy, logp (device
+    tensors of length T; entropy None unless want_entropy). For world == 1, logp/entropy are
+    final; otherwise pass the shards' results to ``merge``."""
+    open(hidden.device.index)
+    req = _request(hidden, weight, target_ids, temperature, bias, loss_mask, cu_seqlens, offset,
+                   real_vocab, padded_vocab, rank, world, want_entropy, status)
+    dev, T = hidden.device, hidden.shape[0]
+    if out is None:
+        out = dict(target_logit=torch.empty(T, dtype=torch.float32, device=dev),
+                   in_range=torch.empty(T, dtype=torch.uint8, device=dev),
+                   lse=torch.empty(T, dtype=torch.float32, device=dev),
+                   entropy=torch.empty(T, dtype=torch.float32, device=dev) if want_entropy else None,
+                   logp=torch.empty(T, dtype=torch.float32, device=dev))
+    o = A.llp_partials(_ptr(out["target_logit"]), _ptr(out["in_range"]), _ptr(out["lse"]),
+                       _ptr(out.get("entropy")), _ptr(out.get("logp")))
+    ws = _workspace(req, A.LLP_OP_FORWARD, dev, workspace)
+    _check(A.load().llp_forward(C.byref(req), C.byref(o), _ptr(ws), ws.numel(),
+                                _stream_ptr(dev)), "llp_forward")
+    return out
+
+
+def merge(parts: Sequence[dict], *, loss_mask: Optional[torch.Tensor] = None,
+          want_entropy: bool = True, status: Optional[torch.Tensor] = None) -> dict:
+    """llp_merge of shard partials given in rank order. Returns logp, lse, entropy."""
+    world = len(parts)
+    if world < 1:
+        raise ValueError("merge needs at least one shard")
+    dev = parts[0]["lse"].device
+    T = parts[0]["lse"].shape[0]
+    open(dev.index)
+    arr = (A.llp_partials * world)()
+    for r, p in enumerate(parts):
+        for k, dt in (("target_logit", torch.float32), ("in_range", torch.uint8),
+                      ("lse", torch.float32)):
+            _need(p[k], f"parts[{r}].{k}", dt, 1, dev)
+            if p[k].shape[0] != T:
+                raise ValueError(f"parts[{r}].{k} length differs")
+        ent = p.get("entropy") if want_entropy else None
+        arr[r] = A.llp_partials(_ptr(p["target_logit"]), _ptr(p["in_range"]), _ptr(p["lse"]),
+                                _ptr(ent), None)
+    out = dict(logp=torch.empty(T, dtype=torch.float32, device=dev),
+               lse=torch.empty(T, dtype=torch.float32, device=dev),
+               entropy=torch.empty(T, dtype=torch.float32, device=dev) if want_entropy else None)
+    fo = A.llp_final_out(_ptr(out["logp"]), _ptr(out["lse"]), _ptr(out["entropy"]))
+    if loss_mask is not None:
+        _need(loss_mask, "loss_mask", torch.uint8, 1, dev)
+    if status is not None:
+        _need(status, "status", torch.int32, 1, dev)
+    _check(A.load().llp_merge(world, arr, T, _ptr(loss_mask), C.byref(fo), _ptr(status),
+                              _stream_ptr(dev)), "llp_merge")
+    return out
+
+
+def backward(hidden: torch.Tensor, weight: torch.Tensor, target_ids: torch.Tensor,
+             lse: torch.Tensor, dlogp: torch.Tensor, *, temperature: float,
+             bias: Optional[torch.Tensor] = None, loss_mask: Optional[torch.Tensor] = None,
+             cu_seqlens: Optional[torch.Tensor] = None, offset: int = 0,
+             real_vocab: Optional[int] = None, padded_vocab: Optional[int] = None,
+             rank: int = 0, world: int = 1, dentropy: Optional[torch.Tensor] = None,
+             entropy: Optional[torch.Tensor] = None, dweight: Optional[torch.Tensor] = None,
+             dbias: Optional[torch.Tensor] = None, want_dbias: Optional[bool] = None,
+             dhidden: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> dict:
+    """llp_backward on one shard: dhidden (bf16, overwritten), dweight (fp32, accumulated),
+    dbias (fp32, accumulated; allocated when the request has a bias or want_dbias)."""
+    open(hidden.device.index)
+    req = _request(hidden, weight, target_ids, temperature, bias, loss_mask, cu_seqlens, offset,
+                   real_vocab, padded_vocab, rank, world, False, status)
+    dev = hidden.device
+    T, H = hidden.shape
+    for name, t in (("lse", lse), ("dlogp", dlogp)):
+        _need(t, name, torch.float32, 1, dev)
+    if dentropy is not None:
+        _need(dentropy, "dentropy", torch.float32, 1, dev)
+        _need(entropy, "entropy", torch.float32, 1, dev)
+    if dhidden is None:
+        dhidden = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if dweight is None:
+        dweight = torch.zeros(weight.shape, dtype=torch.float32, device=dev)
+    _need(dhidden, "dhidden", torch.bfloat16, 2, dev)
+    _need(dweight, "dweight", torch.float32, 2, dev)
+    if want_dbias is None:
+        want_dbias = bias is not None
+    if dbias is None and want_dbias:
+        dbias = torch.zeros(weight.shape[0], dtype=torch.float32, device=dev)
+    bi = A.llp_bwd_in(_ptr(lse), _ptr(dlogp), _ptr(dentropy), _ptr(entropy))
+    bo = A.llp_bwd_out(_ptr(dhidden), dhidden.stride(0) if T > 0 else H, _ptr(dweight),
+                       dweight.stride(0) if weight.shape[0] > 0 else H, _ptr(dbias))
+    ws = _workspace(req, A.LLP_OP_BACKWARD, dev, workspace)
+    _check(A.load().llp_backward(C.byref(req), C.byref(bi), C.byref(bo), _ptr(ws), ws.numel(),
+                                 _stream_ptr(dev)), "llp_backward")
+    return dict(dhidden=dhidden, dweight=dweight, dbias=dbias)
+
+
+def top_p_replay(logits: torch.Tensor, replay_ids: torch.Tensor, target_ids: torch.Tensor, *,
+                 temperature: float, offset: int = 0, real_vocab: Optional[int] = None,
+                 padded_vocab: Optional[int] = None, rank: int = 0, world: int = 1,
+                 loss_mask: Optional[torch.Tensor] = None, processed_logprobs: bool = True,
+                 status: Optional[torch.Tensor] = None, local_size: Optional[int] = None) -> dict:
+    """llp_top_p_replay on one shard's local logits [T, local_size] (fp32 or bf16; a strided
+    view of a wider logits tensor is fine). Returns target_logit, in_range, lse, logp."""
+    dev = logits.device
+    open(dev.index)
+    if logits.dtype not in (torch.float32, torch.bfloat16) or logits.dim() != 2:
+        raise TypeError("logits must be a 2-d fp32 or bf16 tensor")
+    if logits.stride(1) != 1:
+        raise ValueError("logits must be contiguous in its last dimension")
+    _need(replay_ids, "replay_ids", torch.int64, 2, dev)
+    _need(target_ids, "target_ids", torch.int64, 1, dev)
+    T = replay_ids.shape[0]
+    if local_size is None:
+        local_size = logits.shape[1]
+    if padded_vocab is None:
+        padded_vocab = local_size if world == 1 else None
+    if real_vocab is None:
+        real_vocab = padded_vocab
+    if padded_vocab is None:
+        raise ValueError("padded_vocab is required for a vocabulary shard (world > 1)")
+    req = A.llp_topp_request()
+    req.logits = _ptr(logits)
+    req.logits_dtype = A.LLP_DTYPE_F32 if logits.dtype == torch.float32 else A.LLP_DTYPE_BF16
+    req.num_replay = replay_ids.shape[1]
+    req.logits_stride = logits.stride(0) if logits.shape[0] > 0 else local_size
+    req.num_tokens = T
+    req.vocab.offset = int(offset)
+    req.vocab.local_size = int(local_size)
+    req.vocab.real_vocab = int(real_vocab)
+    req.vocab.padded_vocab = int(padded_vocab)
+    req.vocab.rank = int(rank)
+    req.vocab.world = int(world)
+    req.replay_ids = _ptr(replay_ids)
+    req.replay_stride = replay_ids.stride(0) if T > 0 else replay_ids.shape[1]
+    req.target_ids = _ptr(target_ids)
+    if loss_mask is not None:
+        _need(loss_mask, "loss_mask", torch.uint8, 1, dev)
+        req.loss_mask = _ptr(loss_mask)
+    req.temperature = float(temperature)
+    req.processed_logprobs = 1 if processed_logprobs else 0
+    if status is not None:
+        _need(status, "status", torch.int32, 1, dev)
+        req.status_word = _ptr(status)
+    out = dict(target_logit=torch.empty(T, dtype=torch.float32, device=dev),
+               in_range=torch.empty(T, dtype=torch.uint8, device=dev),
+               lse=torch.empty(T, dtype=torch.float32, device=dev), entropy=None,
+               logp=torch.empty(T, dtype=torch.float32, device=dev))
+    o = A.llp_partials(_ptr(out["target_logit"]), _ptr(out["in_range"]), _ptr(out["lse"]), None,
+                       _ptr(out["logp"]))
+    _check(A.load().llp_top_p_replay(C.byref(req), C.byref(o), _stream_ptr(dev)),
+           "llp_top_p_replay")
+    return out

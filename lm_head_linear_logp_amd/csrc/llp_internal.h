@@ -1,0 +1,196 @@
+// llp_internal.h -- kernel argument blocks and launchers shared by the C-ABI host code and
+// the HIP kernels. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "llp.h"
+
+namespace llp {
+
+// Number of fixed K (vocabulary) ranges the dhidden product is split into. Fixed, so that a
+// row's summation order never depends on the batch.
+constexpr int DH_SPLITS = 4;
+constexpr int TILE = 256;  // BM = BN of every GEMM tile
+
+struct LayoutArgs {
+  int64_t T;
+  const uint8_t* mask;
+  const int32_t* cu_seqlens;
+  int32_t num_seqs;
+  int32_t world;
+  const int64_t* targets;
+  int64_t offset, n_real, real_vocab;
+  int32_t* count;   // [1] number of scored rows
+  int32_t* scored;  // [T] compact index -> row
+  int32_t* pos;     // [T] row -> compact index or -1
+  int32_t* tloc;    // [T] compact index -> local target column or -1
+  float* out_t;     // zero outputs of unscored rows (any may be null)
+  uint8_t* out_f;
+  float* out_l;
+  float* out_e;
+  float* out_p;
+  int32_t* status;
+};
+
+struct FwdArgs {
+  const uint16_t* W;
+  int64_t ldw;
+  const uint16_t* h;
+  int64_t ldh;
+  const void* bias;
+  int32_t bias_f32;
+  int32_t H;
+  int64_t n_real;
+  int32_t nvt, ntb;
+  float c1;
+  const int32_t* count;
+  const int32_t* scored;
+  const int32_t* tloc;
+  float* pm;
+  float* ps;
+  float* pq;
+  float* tz;
+  int64_t pstride;  // row capacity of the partial arrays (ntb * 256)
+};
+
+struct CombineArgs {
+  int32_t nvt;
+  int64_t pstride;
+  const int32_t* count;
+  const int32_t* scored;
+  const int32_t* tloc;
+  const float* pm;
+  const float* ps;
+  const float* pq;
+  const float* tz;
+  float* out_t;
+  uint8_t* out_f;
+  float* out_l;
+  float* out_e;
+  float* out_p;
+};
+
+struct MergeArgs {
+  int64_t T;
+  int32_t world;
+  const uint8_t* mask;
+  const float* tl[LLP_MAX_WORLD];
+  const uint8_t* flag[LLP_MAX_WORLD];
+  const float* lse[LLP_MAX_WORLD];
+  const float* ent[LLP_MAX_WORLD];
+  float* out_p;
+  float* out_l;
+  float* out_e;
+  int32_t* status;
+};
+
+struct ToppArgs {
+  int64_t T;
+  const void* logits;
+  int32_t bf16;
+  int32_t K;
+  int64_t lstride;
+  const int64_t* ids;
+  int64_t ids_stride;
+  const int64_t* targets;
+  const uint8_t* mask;
+  int64_t offset, n_real, real_vocab;
+  float c1;
+  float* out_t;
+  uint8_t* out_f;
+  float* out_l;
+  float* out_p;
+  int32_t* status;
+};
+
+struct GradArgs {
+  const uint16_t* W;
+  int64_t ldw;
+  const uint16_t* h;
+  int64_t ldh;
+  const void* bias;
+  int32_t bias_f32;
+  int32_t H;
+  int64_t n_real;
+  int32_t nvt, ntb;
+  float c1;
+  const int32_t* count;
+  const int32_t* scored;
+  const int32_t* tloc;
+  const float* lse;
+  const float* dlogp;
+  const float* dent;
+  const float* ent;
+  uint16_t* G;
+  int64_t ldg;
+};
+
+struct DhArgs {
+  const uint16_t* G;
+  int64_t ldg;
+  const uint16_t* W;
+  int64_t ldw;
+  int64_t n_real;
+  int32_t H;
+  int32_t ntm, ntn, nsplit, nks;
+  const int32_t* count;
+  float* P;
+  int64_t pstride;  // rows per split
+};
+
+struct DhReduceArgs {
+  int64_t T;
+  int32_t H;
+  int32_t nsplit;
+  const int32_t* pos;
+  const float* P;
+  int64_t pstride;
+  uint16_t* dH;
+  int64_t ldd;
+};
+
+struct DwArgs {
+  const uint16_t* G;
+  int64_t ldg;
+  const uint16_t* hg;
+  int32_t H;
+  int32_t ntm, ntn;
+  int64_t n_real;
+  const int32_t* count;
+  float* dW;
+  int64_t lddw;
+};
+
+struct GatherArgs {
+  const uint16_t* h;
+  int64_t ldh;
+  int32_t H;
+  const int32_t* count;
+  const int32_t* scored;
+  uint16_t* hg;
+};
+
+struct DbArgs {
+  const uint16_t* G;
+  int64_t ldg;
+  int64_t n_real;
+  const int32_t* count;
+  float* db;
+};
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int64_t T_cap, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_topp(const ToppArgs& a, hipStream_t s);
+hipError_t launch_grad(const GradArgs& a, hipStream_t s);
+hipError_t launch_dh(const DhArgs& a, hipStream_t s);
+hipError_t launch_dh_reduce(const DhReduceArgs& a, hipStream_t s);
+hipError_t launch_dw(const DwArgs& a, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, int64_t T_cap, hipStream_t s);
+hipError_t launch_dbias(const DbArgs& a, hipStream_t s);
+hipError_t probe_kernels();
+
+}  // namespace llp

@@ -1,0 +1,770 @@
+// llp_kernels.hip -- HIP kernels of the fused linear log-prob operator for gfx950 and their
+// launchers. Every reduction has a fixed order that depends only on vocabulary / K position,
+// never on a row's position in the batch, and no float atomics are used: results are
+// bitwise reproducible and independent of how rows are packed.
+//
+// Sources: [CUDA provider] "feat(rl-kernel): add CUDA linear logp provider integration",
+// [ROCm provider] "feat(rl-kernel): add ROCm linear logp provider integration",
+// [top-p replay] "Perf/cuda compact top p replay".
+#include "llp_internal.h"
+#include "llp_tile.hpp"
+
+#include <math.h>
+
+namespace llp {
+
+// ------------------------------------------------------------------------------------
+// Layout and mask indexing. One workgroup scans the loss mask in order and writes the
+// compact list of scored rows, each row's compact index (-1 when unscored), the target's
+// local column (-1 when outside this shard's real columns), zero outputs for unscored rows,
+// and status bits ([CUDA provider, "Summary"]: the framework keeps token layout and
+// masking; the operator scores unmasked rows only).
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_layout(LayoutArgs a) {
+  __shared__ int wsum[16];
+  __shared__ int carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int status = 0;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < a.T; base += 1024) {
+    const int64_t t = base + tid;
+    const bool in = t < a.T;
+    const bool sc = in && (a.mask == nullptr || a.mask[t] != 0);
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(sc);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    int pre = carry_s;
+    for (int w = 0; w < wave; ++w) pre += wsum[w];
+    const int j = pre + below;
+    if (in) {
+      a.pos[t] = sc ? j : -1;
+      if (sc) {
+        a.scored[j] = (int)t;
+        const int64_t tg = a.targets[t];
+        const bool valid = tg >= 0 && tg < a.real_vocab;
+        if (!valid) status |= LLP_STATUS_TARGET_OUT_OF_RANGE;
+        const int64_t loc = tg - a.offset;
+        const bool hit = valid && loc >= 0 && loc < a.n_real;
+        a.tloc[j] = hit ? (int)loc : -1;
+        if (!hit && a.world == 1) status |= LLP_STATUS_TARGET_NOT_FOUND;
+      } else {
+        if (a.out_t) a.out_t[t] = 0.f;
+        if (a.out_f) a.out_f[t] = 0;
+        if (a.out_l) a.out_l[t] = 0.f;
+        if (a.out_e) a.out_e[t] = 0.f;
+        if (a.out_p) a.out_p[t] = 0.f;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int w = 0; w < 16; ++w) tot += wsum[w];
+      carry_s += tot;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) a.count[0] = carry_s;
+  if (a.cu_seqlens != nullptr) {
+    for (int i = tid; i <= a.num_seqs; i += 1024) {
+      const int c = a.cu_seqlens[i];
+      if (i == 0 && c != 0) status |= LLP_STATUS_LAYOUT_INVALID;
+      if (i == a.num_seqs && (int64_t)c != a.T) status |= LLP_STATUS_LAYOUT_INVALID;
+      if (i < a.num_seqs && a.cu_seqlens[i + 1] < c) status |= LLP_STATUS_LAYOUT_INVALID;
+    }
+  }
+  if (status && a.status) atomicOr(a.status, status);
+}
+
+// ------------------------------------------------------------------------------------
+// Fused forward tile: z = (h W^T + b) * (1/tau) for 256 vocabulary columns x 256 scored
+// rows, then per row of the tile the max m, s = sum exp(z - m) and q = sum exp(z - m) (z - m)
+// log2(e), plus the target logit when the target column lies in the tile. Columns at or
+// past the shard's real vocabulary are excluded ([CUDA provider, "Megatron integration"]:
+// real/padded vocabulary sizes). The [T, V] logits never leave registers.
+// MFMA operand A = weight rows (vocabulary, M), B = hidden rows (tokens, N): each lane owns
+// one token column, so the per-row reductions run down its own registers first.
+// ------------------------------------------------------------------------------------
+template <bool TAIL>
+__device__ __forceinline__ void load_bias16(const void* bias, int bias_f32, int vb, int lane,
+                                            int64_t n_real, float (&b)[16]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int v = vb + mfma_row(r, lane);
+    b[r] = 0.f;
+    if (bias != nullptr && (!TAIL || v < n_real))
+      b[r] = bias_f32 ? reinterpret_cast<const float*>(bias)[v]
+                      : bf16_to_f32(reinterpret_cast<const uint16_t*>(bias)[v]);
+  }
+}
+
+// z of accumulator element r, excluded columns -> -inf. Recomputed where needed so that the
+// 256 scaled logits of a lane are never stored alongside the accumulators.
+template <bool TAIL>
+__device__ __forceinline__ float zval(float acc, const float (&b)[16], int r, bool has_bias,
+                                      float c1, int vrow, int64_t n_real) {
+  const float z = has_bias ? (acc + b[r]) * c1 : acc * c1;
+  return (TAIL && vrow >= n_real) ? -INFINITY : z;
+}
+
+template <bool TAIL>
+__device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const FwdArgs& a, int vt,
+                                             int v0, int j0, int Ts, uint16_t* smem) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int vbase = v0 + wm * 128;
+  const bool hb = a.bias != nullptr;
+  float* red = reinterpret_cast<float*>(smem);  // [6][256]: max0 max1 s0 s1 q0 q1
+  // Pass 1: per-token max over this lane's 64 columns, then over the lane pair (l, l^32),
+  // then over the two waves holding the tile's two column halves.
+  float mx[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) mx[ni] = -INFINITY;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    float b[16];
+    load_bias16<TAIL>(a.bias, a.bias_f32, vbase + mi * 32, lane, a.n_real, b);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        mx[ni] = fmaxf(mx[ni], zval<TAIL>(acc[mi][ni][r], b, r, hb, a.c1,
+                                          vbase + mi * 32 + mfma_row(r, lane), a.n_real));
+  }
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    mx[ni] = fmaxf(mx[ni], __shfl_xor(mx[ni], 32));
+    if (lane < 32) red[wm * 256 + wn * 128 + ni * 32 + lane] = mx[ni];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int tn = wn * 128 + ni * 32 + (lane & 31);
+    mx[ni] = fmaxf(red[tn], red[256 + tn]);
+  }
+  // Pass 2: s = sum 2^d2, q = sum 2^d2 * d2 with d2 = (z - M) log2(e), in register order.
+  float sv[4] = {0.f, 0.f, 0.f, 0.f}, qv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    float b[16];
+    load_bias16<TAIL>(a.bias, a.bias_f32, vbase + mi * 32, lane, a.n_real, b);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float z = zval<TAIL>(acc[mi][ni][r], b, r, hb, a.c1,
+                                   vbase + mi * 32 + mfma_row(r, lane), a.n_real);
+        float d2 = (z - mx[ni]) * kLog2e;
+        if (TAIL) d2 = fmaxf(d2, -1e30f);  // excluded column: exp2 -> 0 and 0 * d2 -> 0
+        const float e = __builtin_amdgcn_exp2f(d2);
+        sv[ni] += e;
+        qv[ni] = fmaf(e, d2, qv[ni]);
+      }
+  }
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    // (x + y) == (y + x): both lanes of a pair hold the same sum.
+    sv[ni] += __shfl_xor(sv[ni], 32);
+    qv[ni] += __shfl_xor(qv[ni], 32);
+    if (lane < 32) {
+      const int tn = wn * 128 + ni * 32 + lane;
+      red[512 + wm * 256 + tn] = sv[ni];
+      red[1024 + wm * 256 + tn] = qv[ni];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int tn = wn * 128 + ni * 32 + (lane & 31);
+    const int j = j0 + tn;
+    if (wm == 0 && lane < 32 && j < Ts) {
+      const int64_t o = (int64_t)vt * a.pstride + j;
+      a.pm[o] = mx[ni];
+      a.ps[o] = red[512 + tn] + red[768 + tn];
+      a.pq[o] = red[1024 + tn] + red[1280 + tn];
+    }
+    // Target logit: the one lane holding column tloc[j] copies its z (rare: skipped unless
+    // some lane of the wave holds a target).
+    const int tl = (j < Ts) ? a.tloc[j] - vbase : -1;
+    const bool mine = tl >= 0 && tl < 128 && (((tl & 31) >> 2) & 1) == (lane >> 5);
+    if (__builtin_amdgcn_ballot_w64(mine)) {
+      const int mt = tl >> 5, rt = (((tl & 31) >> 3) << 2) | (tl & 3);
+      float t = 0.f;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (mi == mt && r == rt) t = acc[mi][ni][r];
+      if (mine) {
+        float bt = 0.f;
+        if (hb) {
+          const int v = vbase + tl;
+          bt = a.bias_f32 ? reinterpret_cast<const float*>(a.bias)[v]
+                          : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[v]);
+        }
+        a.tz[j] = hb ? (t + bt) * a.c1 : t * a.c1;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(NTHREADS, 1) void k_fwd(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[MAIN_LDS_BYTES / 2];
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int vt = tile / a.ntb, tb = tile % a.ntb;
+  const int Ts = *a.count;
+  const int j0 = tb * BN, v0 = vt * BM;
+  if (j0 >= Ts) return;
+  const int t = threadIdx.x, c = t & 7, r0 = t >> 3;
+  LdK la, lb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int v = v0 + r0 + 32 * i;
+    v = v < a.n_real ? v : (int)a.n_real - 1;
+    la.p[i] = a.W + (int64_t)v * a.ldw + c * 8;
+    int j = j0 + r0 + 32 * i;
+    j = j < Ts ? j : Ts - 1;
+    lb.p[i] = a.h + (int64_t)a.scored[j] * a.ldh + c * 8;
+  }
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  mainloop(la, lb, 0, a.H / BK, smem, acc);
+  if (v0 + BM > a.n_real)
+    fwd_epilogue<true>(acc, a, vt, v0, j0, Ts, smem);
+  else
+    fwd_epilogue<false>(acc, a, vt, v0, j0, Ts, smem);
+}
+
+// ------------------------------------------------------------------------------------
+// Cross-tile combine, in vocabulary-tile order: wave w of 16 folds tiles w, w+16, ... for 64
+// rows, then one wave folds the 16 partials in order w = 0..15. With d_k = m_k - M:
+// S = sum_k s_k e^{d_k}, Q = sum_k e^{d_k}(q_k + s_k d_k log2 e); lse = M + ln S and
+// entropy = ln S - ln2 * Q / S. An empty shard gives lse = -inf, entropy 0, target logit 0,
+// in_range 0 and logp -inf ([top-p replay, "Changes" table]: empty vocabulary rows).
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ void fold(float& M, float& S, float& Q, float m, float s, float q) {
+  // Combine (M, S, Q) with a partial (m, s, q); both may be empty (-inf max, zero sums).
+  if (m == -INFINITY) return;
+  if (M == -INFINITY) {
+    M = m; S = s; Q = q;
+    return;
+  }
+  const float N = fmaxf(M, m);
+  const float da = M - N, db = m - N;
+  const float wa = expf(da), wb = expf(db);
+  Q = wa * (Q + S * da * kLog2e) + wb * (q + s * db * kLog2e);
+  S = wa * S + wb * s;
+  M = N;
+}
+
+__global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
+  __shared__ float rm[16][64], rs[16][64], rq[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int Ts = *a.count;
+  const int j = blockIdx.x * 64 + lane;
+  if (blockIdx.x * 64 >= Ts) return;
+  float M = -INFINITY, S = 0.f, Q = 0.f;
+  if (j < Ts) {
+    float mmax = -INFINITY;
+    for (int vt = w; vt < a.nvt; vt += 16) mmax = fmaxf(mmax, a.pm[(int64_t)vt * a.pstride + j]);
+    if (mmax != -INFINITY) {
+      for (int vt = w; vt < a.nvt; vt += 16) {
+        const int64_t o = (int64_t)vt * a.pstride + j;
+        const float d = a.pm[o] - mmax, s = a.ps[o], q = a.pq[o];
+        const float e = expf(d);
+        S += e * s;
+        Q += e * (q + s * d * kLog2e);
+      }
+      M = mmax;
+    }
+  }
+  rm[w][lane] = M;
+  rs[w][lane] = S;
+  rq[w][lane] = Q;
+  __syncthreads();
+  if (w != 0 || j >= Ts) return;
+  M = -INFINITY; S = 0.f; Q = 0.f;
+  for (int g = 0; g < 16; ++g) fold(M, S, Q, rm[g][lane], rs[g][lane], rq[g][lane]);
+  float lse, ent;
+  if (M == -INFINITY || !(S > 0.f)) {
+    lse = -INFINITY;
+    ent = 0.f;
+  } else {
+    const float ls = logf(S);
+    lse = M + ls;
+    ent = ls - kLn2 * (Q / S);
+  }
+  const int row = a.scored[j];
+  const bool hit = a.tloc[j] >= 0;
+  const float tz = hit ? a.tz[j] : 0.f;
+  a.out_t[row] = tz;
+  a.out_f[row] = hit ? 1 : 0;
+  a.out_l[row] = lse;
+  if (a.out_e) a.out_e[row] = ent;
+  if (a.out_p) a.out_p[row] = hit ? tz - lse : -INFINITY;
+}
+
+// ------------------------------------------------------------------------------------
+// Rank-ordered shard merge ([top-p replay, "Summary"]: rank-ordered reductions, shards with
+// no candidates handled). One thread per row; shards r = 0..world-1 in order.
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.T) return;
+  if (a.mask != nullptr && a.mask[t] == 0) {
+    a.out_p[t] = 0.f;
+    a.out_l[t] = 0.f;
+    if (a.out_e) a.out_e[t] = 0.f;
+    return;
+  }
+  float M = -INFINITY;
+  for (int r = 0; r < a.world; ++r) M = fmaxf(M, a.lse[r][t]);
+  float lse = -INFINITY;
+  if (M != -INFINITY) {
+    float S = 0.f;
+    for (int r = 0; r < a.world; ++r) {
+      const float L = a.lse[r][t];
+      if (L != -INFINITY) S += expf(L - M);
+    }
+    lse = M + logf(S);
+  }
+  int found = -1;
+  for (int r = 0; r < a.world && found < 0; ++r)
+    if (a.flag[r][t]) found = r;
+  if (found >= 0) {
+    a.out_p[t] = a.tl[found][t] - lse;
+  } else {
+    a.out_p[t] = -INFINITY;
+    if (a.status) atomicOr(a.status, LLP_STATUS_TARGET_NOT_FOUND);
+  }
+  a.out_l[t] = lse;
+  if (a.out_e) {
+    float ent = 0.f;
+    if (lse != -INFINITY)
+      for (int r = 0; r < a.world; ++r) {
+        const float L = a.lse[r][t];
+        if (L != -INFINITY) ent += expf(L - lse) * (a.ent[r][t] + (lse - L));
+      }
+    a.out_e[t] = ent;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Compact top-p replay scorer ([top-p replay, "Summary"] and "Changes" table: validate the
+// replay inputs, sort and deduplicate up to 64 ids, apply temperature, return local
+// reductions; score the compact ids directly, no full-vocabulary keep mask). One wave64 per
+// row: lane k holds slot k; ids inside the shard's real range become local keys, the rest a
+// sentinel; a bitonic sort across lanes, adjacent dedup, and compaction by ballot put the
+// i-th distinct id on lane i, so the fixed butterfly sum is independent of the order and
+// multiplicity of the listed ids.
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_topp(ToppArgs a) {
+  __shared__ float zs[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + w;
+  if (row >= a.T) return;
+  int status = 0;
+  int64_t id = -1;
+  if (lane < a.K) id = a.ids[row * a.ids_stride + lane];
+  if (id < -1 || id >= a.real_vocab) {
+    status |= LLP_STATUS_REPLAY_ID_INVALID;
+    id = -1;
+  }
+  const bool scored = a.mask == nullptr || a.mask[row] != 0;
+  if (!scored) {
+    if (lane == 0) {
+      a.out_t[row] = 0.f;
+      a.out_f[row] = 0;
+      a.out_l[row] = 0.f;
+      if (a.out_p) a.out_p[row] = 0.f;
+    }
+    if (status && a.status) atomicOr(a.status, status);
+    return;
+  }
+  const int64_t loc = id - a.offset;
+  int key = (id >= 0 && loc >= 0 && loc < a.n_real) ? (int)loc : 0x7FFFFFFF;
+  // Bitonic sort, ascending over lane index.
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      const int other = __shfl_xor(key, jj);
+      const bool up = (lane & k) == 0;
+      const bool lower = (lane & jj) == 0;
+      const int lo = min(key, other), hi = max(key, other);
+      key = (lower == up) ? lo : hi;
+    }
+  }
+  const int prev = __shfl_up(key, 1);
+  const bool keep = key != 0x7FFFFFFF && (lane == 0 || key != prev);
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+  const int n = __popcll(bal);
+  const int p = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+  const int64_t tg = a.targets[row];
+  if (tg < 0 || tg >= a.real_vocab) status |= LLP_STATUS_TARGET_OUT_OF_RANGE;
+  const int64_t tloc = tg - a.offset;
+  float x = 0.f;
+  if (keep) {
+    const int64_t o = row * a.lstride + key;
+    x = a.bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.logits)[o])
+               : reinterpret_cast<const float*>(a.logits)[o];
+    zs[w][p] = x * a.c1;
+  }
+  const bool has_t = keep && (int64_t)key == tloc;
+  const uint64_t tb = __builtin_amdgcn_ballot_w64(has_t);
+  // zs[w] is private to this wave; one wave's LDS accesses complete in issue order.
+  __builtin_amdgcn_wave_barrier();
+  const float z = lane < n ? zs[w][lane] : -INFINITY;
+  float M = z;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float e = lane < n ? expf(z - M) : 0.f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) e += __shfl_xor(e, off);
+  if (lane == 0) {
+    if (n == 0) {
+      a.out_t[row] = 0.f;
+      a.out_f[row] = 0;
+      a.out_l[row] = -INFINITY;
+      if (a.out_p) a.out_p[row] = -INFINITY;
+    } else {
+      const float lse = M + logf(e);
+      float t = 0.f;
+      // The target's compact position = kept lanes below the (single) lane holding it.
+      if (tb) t = zs[w][__popcll(bal & ((tb & (0 - tb)) - 1))];
+      a.out_t[row] = tb ? t : 0.f;
+      a.out_f[row] = tb ? 1 : 0;
+      a.out_l[row] = lse;
+      if (a.out_p) a.out_p[row] = tb ? t - lse : -INFINITY;
+    }
+  }
+  if (a.status) {
+    const uint64_t any = __builtin_amdgcn_ballot_w64(status != 0);
+    if (any) {
+      int st = status;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) st |= __shfl_xor(st, off);
+      if (lane == 0) atomicOr(a.status, st);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Backward. G[j, v] = (dlogp (1[v = target] - p) - dentropy p (z - E_p z)) / tau with
+// p = exp(z - lse) is recomputed tile by tile with the forward's tile, rounded to bf16 and
+// written as G[scored row j][local column v] (zeros in excluded columns). Then
+// dhidden = G W (split over K = vocabulary in a fixed number of fixed ranges, partials
+// summed in range order) and dweight += G^T h over the scored rows in order, db += sum_j G.
+// ------------------------------------------------------------------------------------
+constexpr int GT_STRIDE = BN + 8;  // padded LDS row (bf16 elements) of the staged G tile
+constexpr int GRAD_LDS_BYTES = BN * GT_STRIDE * 2;
+constexpr int BWDG_LDS_BYTES = GRAD_LDS_BYTES > MAIN_LDS_BYTES ? GRAD_LDS_BYTES : MAIN_LDS_BYTES;
+
+template <bool TAIL>
+__device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArgs& a, int v0,
+                                              int j0, int Ts, uint16_t* smem) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int vbase = v0 + wm * 128;
+  float lse[4], dl[4], de[4], ez[4];
+  int tl[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int j = j0 + wn * 128 + ni * 32 + (lane & 31);
+    const int jj = j < Ts ? j : Ts - 1;
+    const int row = a.scored[jj];
+    lse[ni] = a.lse[row];
+    dl[ni] = a.dlogp[row];
+    de[ni] = a.dent ? a.dent[row] : 0.f;
+    ez[ni] = a.dent ? lse[ni] - a.ent[row] : 0.f;
+    tl[ni] = a.tloc[jj] - vbase;
+  }
+  // Stage the bf16 tile as Gs[token][vocab] in LDS, then write full rows.
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    float b[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int v = vbase + mi * 32 + mfma_row(r, lane);
+      b[r] = 0.f;
+      if (a.bias != nullptr && v < a.n_real)
+        b[r] = a.bias_f32 ? reinterpret_cast<const float*>(a.bias)[v]
+                          : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[v]);
+    }
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int tn = wn * 128 + ni * 32 + (lane & 31);
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        uint32_t pk[2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = rg * 4 + u;
+          const int vl = mi * 32 + mfma_row(r, lane);
+          const float z = a.bias != nullptr ? (acc[mi][ni][r] + b[r]) * a.c1 : acc[mi][ni][r] * a.c1;
+          const float p = __builtin_amdgcn_exp2f((z - lse[ni]) * kLog2e);
+          float g = dl[ni] * ((vl == tl[ni] ? 1.f : 0.f) - p);
+          if (a.dent) g -= de[ni] * p * (z - ez[ni]);
+          g *= a.c1;
+          if (TAIL && vbase + vl >= a.n_real) g = 0.f;
+          const uint32_t hb = f32_to_bf16_rne(g);
+          if (u & 1)
+            pk[u >> 1] |= hb << 16;
+          else
+            pk[u >> 1] = hb;
+        }
+        const int vl0 = wm * 128 + mi * 32 + mfma_row(rg * 4, lane);
+        *reinterpret_cast<uint2*>(smem + tn * GT_STRIDE + vl0) = make_uint2(pk[0], pk[1]);
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < BN * (BM / 8); idx += NTHREADS) {
+    const int tn = idx >> 5, c = idx & 31;
+    const int j = j0 + tn;
+    if (j < Ts)
+      *reinterpret_cast<u32x4*>(a.G + (int64_t)j * a.ldg + v0 + c * 8) =
+          *reinterpret_cast<const u32x4*>(smem + tn * GT_STRIDE + c * 8);
+  }
+}
+
+__global__ __launch_bounds__(NTHREADS, 1) void k_grad(GradArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[BWDG_LDS_BYTES / 2];
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int vt = tile / a.ntb, tb = tile % a.ntb;
+  const int Ts = *a.count;
+  const int j0 = tb * BN, v0 = vt * BM;
+  if (j0 >= Ts) return;
+  const int t = threadIdx.x, c = t & 7, r0 = t >> 3;
+  LdK la, lb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int v = v0 + r0 + 32 * i;
+    v = v < a.n_real ? v : (int)a.n_real - 1;
+    la.p[i] = a.W + (int64_t)v * a.ldw + c * 8;
+    int j = j0 + r0 + 32 * i;
+    j = j < Ts ? j : Ts - 1;
+    lb.p[i] = a.h + (int64_t)a.scored[j] * a.ldh + c * 8;
+  }
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  mainloop(la, lb, 0, a.H / BK, smem, acc);
+  if (v0 + BM > a.n_real)
+    grad_epilogue<true>(acc, a, v0, j0, Ts, smem);
+  else
+    grad_epilogue<false>(acc, a, v0, j0, Ts, smem);
+}
+
+// Rows of the weight as the K operand of dhidden = G W: W[k, n0 + 8 mb .. +7].
+struct WRows {
+  const uint16_t* W;
+  int64_t ldw;
+  int n_real;
+  int col;
+  __device__ __forceinline__ const uint16_t* operator()(int k) const {
+    return k < n_real ? W + (int64_t)k * ldw + col : nullptr;
+  }
+};
+
+// dhidden partials: P[split][j][n] = sum over the split's K range of G[j, k] W[k, n].
+__global__ __launch_bounds__(NTHREADS, 1) void k_dh(DhArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[MAIN_LDS_BYTES / 2];
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  // Logical order: split, then N tile, then M tile fastest.
+  const int mt = tile % a.ntm;
+  const int nt = (tile / a.ntm) % a.ntn;
+  const int sp = tile / (a.ntm * a.ntn);
+  const int Ts = *a.count;
+  const int j0 = mt * BM, n0 = nt * BN;
+  if (j0 >= Ts) return;
+  const int t = threadIdx.x, c = t & 7, r0 = t >> 3;
+  LdK la;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) la.p[i] = a.G + (int64_t)(j0 + r0 + 32 * i) * a.ldg + c * 8;
+  int col = n0 + (t & 31) * 8;
+  col = col <= a.H - 8 ? col : a.H - 8;
+  LdMN<WRows> lb{WRows{a.W, a.ldw, (int)a.n_real, col}};
+  const int ks0 = (int)((int64_t)a.nks * sp / a.nsplit);
+  const int ks1 = (int)((int64_t)a.nks * (sp + 1) / a.nsplit);
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  mainloop(la, lb, ks0, ks1, smem, acc);
+  const int lane = t & 63, wave = t >> 6, wm = wave & 1, wn = wave >> 1;
+  float* P = a.P + (int64_t)sp * a.pstride * a.H;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int n = n0 + wn * 128 + ni * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + wm * 128 + mi * 32 + mfma_row(r, lane);
+        if (j < Ts && n < a.H) P[(int64_t)j * a.H + n] = acc[mi][ni][r];
+      }
+    }
+}
+
+// dhidden[row] = bf16(sum over splits in order); unscored rows are zero.
+__global__ __launch_bounds__(256) void k_dh_reduce(DhReduceArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cpr = a.H / 8;  // 8-column chunks per row
+  if (idx >= a.T * cpr) return;
+  const int64_t t = idx / cpr;
+  const int n = (int)(idx % cpr) * 8;
+  const int j = a.pos[t];
+  uint32_t pk[4] = {0u, 0u, 0u, 0u};
+  if (j >= 0) {
+    float s[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s[u] = 0.f;
+    for (int sp = 0; sp < a.nsplit; ++sp) {
+      const float* P = a.P + ((int64_t)sp * a.pstride + j) * a.H + n;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s[u] += P[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      pk[u] = (uint32_t)f32_to_bf16_rne(s[2 * u]) | ((uint32_t)f32_to_bf16_rne(s[2 * u + 1]) << 16);
+  }
+  *reinterpret_cast<u32x4*>(a.dH + t * a.ldd + n) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+}
+
+// Rows of G (K = scored token) restricted to 8 vocabulary columns, zero past the count.
+struct GRows {
+  const uint16_t* G;
+  int64_t ldg;
+  int Ts;
+  int col;
+  __device__ __forceinline__ const uint16_t* operator()(int k) const {
+    return k < Ts ? G + (int64_t)k * ldg + col : nullptr;
+  }
+};
+
+// dweight[v, n] += sum_j G[j, v] hg[j, n] over the scored rows j in order.
+__global__ __launch_bounds__(NTHREADS, 1) void k_dw(DwArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[MAIN_LDS_BYTES / 2];
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int nt = tile % a.ntn, mt = tile / a.ntn;
+  const int Ts = *a.count;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int t = threadIdx.x;
+  int ncol = n0 + (t & 31) * 8;
+  ncol = ncol <= a.H - 8 ? ncol : a.H - 8;
+  LdMN<GRows> la{GRows{a.G, a.ldg, Ts, m0 + (t & 31) * 8}};
+  LdMN<GRows> lb{GRows{a.hg, (int64_t)a.H, Ts, ncol}};
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  mainloop(la, lb, 0, (Ts + BK - 1) / BK, smem, acc);
+  const int lane = t & 63, wave = t >> 6, wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int n = n0 + wn * 128 + ni * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = m0 + wm * 128 + mi * 32 + mfma_row(r, lane);
+        if (v < a.n_real && n < a.H) {
+          float* d = a.dW + (int64_t)v * a.lddw + n;
+          *d = *d + acc[mi][ni][r];
+        }
+      }
+    }
+}
+
+// hg[j] = hidden[scored[j]] (compact copy of the scored rows for the dweight product).
+__global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
+  const int Ts = *a.count;
+  const int64_t cpr = a.H / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)Ts * cpr) return;
+  const int64_t j = idx / cpr;
+  const int n = (int)(idx % cpr) * 8;
+  *reinterpret_cast<u32x4*>(a.hg + j * a.H + n) =
+      *reinterpret_cast<const u32x4*>(a.h + (int64_t)a.scored[j] * a.ldh + n);
+}
+
+// dbias[v] += sum_j G[j, v] over scored rows in order.
+__global__ __launch_bounds__(256) void k_dbias(DbArgs a) {
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= a.n_real) return;
+  const int Ts = *a.count;
+  float s = 0.f;
+  for (int j = 0; j < Ts; ++j) s += bf16_to_f32(a.G[(int64_t)j * a.ldg + v]);
+  a.db[v] += s;
+}
+
+// ------------------------------------------------------------------------------------
+// Launchers (host). Each returns the launch status.
+// ------------------------------------------------------------------------------------
+static inline int ceil_div64(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_layout, dim3(1), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
+  if (a.nvt > 0 && a.ntb > 0) hipLaunchKernelGGL(k_fwd, dim3(a.nvt * a.ntb), dim3(NTHREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, int64_t T_cap, hipStream_t s) {
+  if (T_cap > 0) hipLaunchKernelGGL(k_combine, dim3(ceil_div64(T_cap, 64)), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
+  if (a.T > 0) hipLaunchKernelGGL(k_merge, dim3(ceil_div64(a.T, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topp(const ToppArgs& a, hipStream_t s) {
+  if (a.T > 0) hipLaunchKernelGGL(k_topp, dim3(ceil_div64(a.T, 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad(const GradArgs& a, hipStream_t s) {
+  if (a.nvt > 0 && a.ntb > 0) hipLaunchKernelGGL(k_grad, dim3(a.nvt * a.ntb), dim3(NTHREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dh(const DhArgs& a, hipStream_t s) {
+  const int n = a.ntm * a.ntn * a.nsplit;
+  if (n > 0) hipLaunchKernelGGL(k_dh, dim3(n), dim3(NTHREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dh_reduce(const DhReduceArgs& a, hipStream_t s) {
+  const int64_t n = a.T * (a.H / 8);
+  if (n > 0) hipLaunchKernelGGL(k_dh_reduce, dim3(ceil_div64(n, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw(const DwArgs& a, hipStream_t s) {
+  const int n = a.ntm * a.ntn;
+  if (n > 0) hipLaunchKernelGGL(k_dw, dim3(n), dim3(NTHREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, int64_t T_cap, hipStream_t s) {
+  const int64_t n = T_cap * (a.H / 8);
+  if (n > 0) hipLaunchKernelGGL(k_gather, dim3(ceil_div64(n, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dbias(const DbArgs& a, hipStream_t s) {
+  if (a.n_real > 0) hipLaunchKernelGGL(k_dbias, dim3(ceil_div64(a.n_real, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t probe_kernels() {
+  hipFuncAttributes attr;
+  return hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(k_fwd));
+}
+
+}  // namespace llp

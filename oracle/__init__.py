@@ -51,7 +51,7 @@ def as_f64(x) -> np.ndarray | None:
     x = np.asarray(x)
     if x.dtype == np.uint16:
         return bf16_to_f64(x)
-    return x.astype(np.float64)
+    return x if x.dtype == np.float64 else x.astype(np.float64)
 
 
 def logits(h: np.ndarray, w_rows: np.ndarray, bias_rows, temperature: float) -> np.ndarray:

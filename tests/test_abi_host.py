@@ -1,0 +1,267 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* the library loads and exports every function include/llp.h declares;
+* the ctypes mirror has the header's struct sizes and field offsets (gcc-compiled probe);
+* malformed requests are rejected with LLP_ERR_INVALID_ARGUMENT / LLP_ERR_UNSUPPORTED before
+  anything touches a device; llp_open without a gfx950 device returns LLP_ERR_UNAVAILABLE;
+* llp_workspace_bytes is a pure function of the shapes.
+"""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from lm_head_linear_logp_amd import _capi as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llp.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(A.LIB_PATH),
+                                reason="libllp.so not built (python -m lm_head_linear_logp_amd.build)")
+
+FAKE = 0x100000  # aligned, never dereferenced by validation
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"LLP_API\s+[\w\s\*]+?\b(llp_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(A.SIGNATURES), names
+    lib = C.CDLL(A.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+STRUCTS = ["llp_info", "llp_projection", "llp_vocab_partition", "llp_token_layout",
+           "llp_request", "llp_partials", "llp_final_out", "llp_bwd_in", "llp_bwd_out",
+           "llp_topp_request"]
+
+
+def test_ctypes_mirror_matches_header(tmp_path):
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "llp.h"', "int main(void){"]
+    for s in STRUCTS:
+        lines.append(f'printf("{s} size %zu\\n", sizeof({s}));')
+        for f, _ in getattr(A, s)._fields_:
+            lines.append(f'printf("{s} {f} %zu\\n", offsetof({s}, {f}));')
+    lines.append("return 0;}")
+    src = tmp_path / "probe.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    got = {}
+    for ln in out.splitlines():
+        s, f, v = ln.split()
+        got[(s, f)] = int(v)
+    for s in STRUCTS:
+        cs = getattr(A, s)
+        assert got[(s, "size")] == C.sizeof(cs), s
+        for f, _ in cs._fields_:
+            assert got[(s, f)] == getattr(cs, f).offset, (s, f)
+
+
+def test_header_constants_match():
+    src = open(HEADER).read()
+    for name in ("LLP_MAX_REPLAY_IDS", "LLP_MAX_WORLD"):
+        assert int(re.search(rf"#define {name} (\d+)", src).group(1)) == getattr(A, name)
+    for name in ("LLP_STATUS_TARGET_OUT_OF_RANGE", "LLP_STATUS_TARGET_NOT_FOUND",
+                 "LLP_STATUS_REPLAY_ID_INVALID", "LLP_STATUS_LAYOUT_INVALID",
+                 "LLP_ERR_UNAVAILABLE", "LLP_ERR_INVALID_ARGUMENT", "LLP_ERR_UNSUPPORTED",
+                 "LLP_DTYPE_BF16", "LLP_DTYPE_F32", "LLP_OP_FORWARD", "LLP_OP_BACKWARD",
+                 "LLP_FLAG_WANT_ENTROPY"):
+        assert int(re.search(rf"\b{name} = (\d+)", src).group(1)) == getattr(A, name), name
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_present(), reason="a GPU is present")
+def test_open_without_device_is_unavailable():
+    lib = A.load()
+    info = A.llp_info()
+    assert lib.llp_open(0, C.byref(info)) == A.LLP_ERR_UNAVAILABLE
+    assert lib.llp_last_error()
+
+
+def good_request(T=4096, H=4096, V=151936, Vr=151669):
+    r = A.llp_request()
+    r.proj.hidden, r.proj.hidden_stride = FAKE, H
+    r.proj.weight, r.proj.weight_stride = FAKE, H
+    r.proj.hidden_size = H
+    r.vocab.offset, r.vocab.local_size, r.vocab.real_vocab, r.vocab.padded_vocab = 0, V, Vr, V
+    r.vocab.rank, r.vocab.world = 0, 1
+    r.layout.num_tokens = T
+    r.target_ids = FAKE
+    r.temperature = 0.7
+    return r
+
+
+def good_out():
+    return A.llp_partials(FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def call_forward(req, out=None, ws_bytes=1 << 40, ws=FAKE):
+    lib = A.load()
+    return lib.llp_forward(C.byref(req), C.byref(out or good_out()), ws, ws_bytes, None)
+
+
+def _mut(fn):
+    r = good_request()
+    fn(r)
+    return r
+
+
+BAD_FORWARD = [
+    ("negative T", lambda r: setattr(r.layout, "num_tokens", -1), A.LLP_ERR_INVALID_ARGUMENT),
+    ("H not multiple of 64", lambda r: (setattr(r.proj, "hidden_size", 4000),
+                                        setattr(r.proj, "hidden_stride", 4000),
+                                        setattr(r.proj, "weight_stride", 4000)), A.LLP_ERR_UNSUPPORTED),
+    ("hidden stride < H", lambda r: setattr(r.proj, "hidden_stride", 4095), A.LLP_ERR_INVALID_ARGUMENT),
+    ("weight stride odd", lambda r: setattr(r.proj, "weight_stride", 4097), A.LLP_ERR_INVALID_ARGUMENT),
+    ("hidden misaligned", lambda r: setattr(r.proj, "hidden", FAKE + 2), A.LLP_ERR_INVALID_ARGUMENT),
+    ("weight NULL", lambda r: setattr(r.proj, "weight", None), A.LLP_ERR_INVALID_ARGUMENT),
+    ("targets NULL", lambda r: setattr(r, "target_ids", None), A.LLP_ERR_INVALID_ARGUMENT),
+    ("tau zero", lambda r: setattr(r, "temperature", 0.0), A.LLP_ERR_INVALID_ARGUMENT),
+    ("tau negative", lambda r: setattr(r, "temperature", -1.0), A.LLP_ERR_INVALID_ARGUMENT),
+    ("tau nan", lambda r: setattr(r, "temperature", float("nan")), A.LLP_ERR_INVALID_ARGUMENT),
+    ("tau inf", lambda r: setattr(r, "temperature", float("inf")), A.LLP_ERR_INVALID_ARGUMENT),
+    ("real > padded", lambda r: setattr(r.vocab, "real_vocab", 151937), A.LLP_ERR_INVALID_ARGUMENT),
+    ("real zero", lambda r: setattr(r.vocab, "real_vocab", 0), A.LLP_ERR_INVALID_ARGUMENT),
+    ("world1 partial shard", lambda r: setattr(r.vocab, "local_size", 1000), A.LLP_ERR_INVALID_ARGUMENT),
+    ("shard past padded", lambda r: (setattr(r.vocab, "world", 4), setattr(r.vocab, "offset", 120000),
+                                     setattr(r.vocab, "local_size", 37984)), A.LLP_ERR_INVALID_ARGUMENT),
+    ("rank >= world", lambda r: (setattr(r.vocab, "world", 4), setattr(r.vocab, "rank", 4),
+                                 setattr(r.vocab, "local_size", 37984)), A.LLP_ERR_INVALID_ARGUMENT),
+    ("world too big", lambda r: setattr(r.vocab, "world", 65), A.LLP_ERR_INVALID_ARGUMENT),
+    ("bad bias dtype", lambda r: (setattr(r.proj, "bias", FAKE), setattr(r.proj, "bias_dtype", 7)),
+     A.LLP_ERR_INVALID_ARGUMENT),
+    ("unknown flag", lambda r: setattr(r, "flags", 2), A.LLP_ERR_INVALID_ARGUMENT),
+]
+
+
+@pytest.mark.parametrize("name,fn,code", BAD_FORWARD, ids=[b[0] for b in BAD_FORWARD])
+def test_forward_rejects_malformed_request(name, fn, code):
+    assert call_forward(_mut(fn)) == code
+    assert A.load().llp_last_error()
+
+
+def test_forward_rejects_bad_outputs_and_workspace():
+    r = good_request()
+    assert call_forward(r, A.llp_partials(None, FAKE, FAKE, FAKE, FAKE)) == A.LLP_ERR_INVALID_ARGUMENT
+    r.flags = A.LLP_FLAG_WANT_ENTROPY
+    assert call_forward(r, A.llp_partials(FAKE, FAKE, FAKE, None, FAKE)) == A.LLP_ERR_INVALID_ARGUMENT
+    r.layout.num_tokens = 0          # no rows: output pointers may be NULL
+    assert call_forward(r, A.llp_partials(None, None, None, None, None)) != A.LLP_ERR_INVALID_ARGUMENT
+    r.layout.num_tokens = 4096
+    r.flags = 0
+    assert call_forward(r, ws_bytes=1000) == A.LLP_ERR_INVALID_ARGUMENT
+    assert call_forward(r, ws=FAKE + 16) == A.LLP_ERR_INVALID_ARGUMENT
+    lib = A.load()
+    assert lib.llp_forward(None, C.byref(good_out()), FAKE, 1 << 40, None) == A.LLP_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.skipif(_gpu_present(), reason="a GPU is present")
+def test_valid_request_passes_validation():
+    """A well-formed request gets past validation; without a device it fails afterwards."""
+    st = call_forward(good_request())
+    assert st not in (A.LLP_OK, A.LLP_ERR_INVALID_ARGUMENT) or "llp_open" in A.load().llp_last_error().decode()
+
+
+def test_workspace_bytes_pure_function():
+    lib = A.load()
+    n1, n2 = C.c_size_t(), C.c_size_t()
+    r = good_request()
+    assert lib.llp_workspace_bytes(C.byref(r), A.LLP_OP_FORWARD, C.byref(n1)) == A.LLP_OK
+    assert lib.llp_workspace_bytes(C.byref(r), A.LLP_OP_FORWARD, C.byref(n2)) == A.LLP_OK
+    assert n1.value == n2.value
+    # 593 vocabulary tiles x 4096 rows x 3 fp32 partials dominate the forward workspace.
+    assert 593 * 4096 * 12 <= n1.value < 593 * 4096 * 12 + (1 << 20)
+    nb = C.c_size_t()
+    assert lib.llp_workspace_bytes(C.byref(r), A.LLP_OP_BACKWARD, C.byref(nb)) == A.LLP_OK
+    assert nb.value >= 4096 * 593 * 256 * 2          # the bf16 G buffer
+    assert lib.llp_workspace_bytes(C.byref(r), 3, C.byref(nb)) == A.LLP_ERR_INVALID_ARGUMENT
+
+
+def _merge(world, parts, T=16, out=None):
+    lib = A.load()
+    arr = (A.llp_partials * max(world, 1))(*parts) if parts else None
+    fo = out or A.llp_final_out(FAKE, FAKE, None)
+    return lib.llp_merge(world, arr, T, None, C.byref(fo), None, None)
+
+
+def test_merge_validation():
+    p = A.llp_partials(FAKE, FAKE, FAKE, None, None)
+    assert _merge(0, [p]) == A.LLP_ERR_INVALID_ARGUMENT
+    assert _merge(65, [p] * 65) == A.LLP_ERR_INVALID_ARGUMENT
+    assert _merge(2, [p, A.llp_partials(FAKE, None, FAKE, None, None)]) == A.LLP_ERR_INVALID_ARGUMENT
+    # entropy requested but a part has none
+    assert _merge(2, [p, p], out=A.llp_final_out(FAKE, FAKE, FAKE)) == A.LLP_ERR_INVALID_ARGUMENT
+    assert _merge(1, [p], out=A.llp_final_out(None, FAKE, None)) == A.LLP_ERR_INVALID_ARGUMENT
+
+
+def good_topp():
+    q = A.llp_topp_request()
+    q.logits, q.logits_dtype, q.num_replay, q.logits_stride = FAKE, A.LLP_DTYPE_F32, 64, 151936
+    q.num_tokens = 4096
+    q.vocab.offset, q.vocab.local_size, q.vocab.real_vocab, q.vocab.padded_vocab = 0, 151936, 151669, 151936
+    q.vocab.rank, q.vocab.world = 0, 1
+    q.replay_ids, q.replay_stride, q.target_ids = FAKE, 64, FAKE
+    q.temperature, q.processed_logprobs = 0.7, 1
+    return q
+
+
+BAD_TOPP = [
+    ("raw logprobs mode", lambda q: setattr(q, "processed_logprobs", 0)),
+    ("K = 65", lambda q: (setattr(q, "num_replay", 65), setattr(q, "replay_stride", 65))),
+    ("K = 0", lambda q: setattr(q, "num_replay", 0)),
+    ("replay stride < K", lambda q: setattr(q, "replay_stride", 32)),
+    ("bad dtype", lambda q: setattr(q, "logits_dtype", 9)),
+    ("logits stride < local", lambda q: setattr(q, "logits_stride", 1000)),
+    ("tau zero", lambda q: setattr(q, "temperature", 0.0)),
+    ("ids NULL", lambda q: setattr(q, "replay_ids", None)),
+    ("bad partition", lambda q: setattr(q.vocab, "real_vocab", 200000)),
+]
+
+
+@pytest.mark.parametrize("name,fn", BAD_TOPP, ids=[b[0] for b in BAD_TOPP])
+def test_topp_rejects_malformed_request(name, fn):
+    q = good_topp()
+    fn(q)
+    o = A.llp_partials(FAKE, FAKE, FAKE, None, FAKE)
+    assert A.load().llp_top_p_replay(C.byref(q), C.byref(o), None) == A.LLP_ERR_INVALID_ARGUMENT
+
+
+def test_topp_rejects_entropy_output():
+    q = good_topp()
+    o = A.llp_partials(FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert A.load().llp_top_p_replay(C.byref(q), C.byref(o), None) == A.LLP_ERR_INVALID_ARGUMENT
+
+
+def test_backward_validation():
+    lib = A.load()
+    r = good_request()
+    bi = A.llp_bwd_in(FAKE, FAKE, None, None)
+    bo = A.llp_bwd_out(FAKE, 4096, FAKE, 4096, None)
+    call = lambda: lib.llp_backward(C.byref(r), C.byref(bi), C.byref(bo), FAKE, 1 << 40, None)
+    bi.dentropy = FAKE   # dentropy without entropy
+    assert call() == A.LLP_ERR_INVALID_ARGUMENT
+    bi.dentropy = None
+    bo.dhidden_stride = 100
+    assert call() == A.LLP_ERR_INVALID_ARGUMENT
+    bo.dhidden_stride = 4096
+    bo.dweight = None
+    assert call() == A.LLP_ERR_INVALID_ARGUMENT
+    bo.dweight = FAKE
+    bi.lse = None
+    assert call() == A.LLP_ERR_INVALID_ARGUMENT
