@@ -95,7 +95,9 @@ SIGNATURES = {
     "llp_last_error": (C.c_char_p, []),
 }
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllp.so")
+# The in-tree build; LLP_LIBRARY may name another build of the same sources.
+LIB_PATH = os.environ.get("LLP_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libllp.so")
 _lib = None
 
 

@@ -210,27 +210,30 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const Fw
   }
 }
 
-__global__ __launch_bounds__(NTHREADS, 1) void k_fwd(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[MAIN_LDS_BYTES / 2];
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int vt = tile / a.ntb, tb = tile % a.ntb;
+// The epilogue reuses the pipeline's LDS for 6 x 256 fp32 partials.
+static_assert(6 * 256 * 4 <= dma::LDS_BYTES, "forward epilogue LDS");
+
+__global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
+  int vt, tb;
+  vocab_token_tile(xcd_remap(blockIdx.x, gridDim.x), a.nvt, a.ntb, vt, tb);
   const int Ts = *a.count;
   const int j0 = tb * BN, v0 = vt * BM;
   if (j0 >= Ts) return;
-  const int t = threadIdx.x, c = t & 7, r0 = t >> 3;
-  LdK la, lb;
+  dma::Loader la, lb;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int v = v0 + r0 + 32 * i;
+  for (int u = 0; u < 4; ++u) {
+    const int r = dma::Loader::row_of(u), c = dma::Loader::chunk_of(u);
+    int v = v0 + r;
     v = v < a.n_real ? v : (int)a.n_real - 1;
-    la.p[i] = a.W + (int64_t)v * a.ldw + c * 8;
-    int j = j0 + r0 + 32 * i;
+    la.p[u] = a.W + (int64_t)v * a.ldw + c * 8;
+    int j = j0 + r;
     j = j < Ts ? j : Ts - 1;
-    lb.p[i] = a.h + (int64_t)a.scored[j] * a.ldh + c * 8;
+    lb.p[u] = a.h + (int64_t)a.scored[j] * a.ldh + c * 8;
   }
   f32x16 acc[4][4];
   zero_acc(acc);
-  mainloop(la, lb, 0, a.H / BK, smem, acc);
+  dma::mainloop(la, lb, 0, a.H / dma::BKD, smem, acc);
   if (v0 + BM > a.n_real)
     fwd_epilogue<true>(acc, a, vt, v0, j0, Ts, smem);
   else
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(256) void k_topp(ToppArgs a) {
 // ------------------------------------------------------------------------------------
 constexpr int GT_STRIDE = BN + 8;  // padded LDS row (bf16 elements) of the staged G tile
 constexpr int GRAD_LDS_BYTES = BN * GT_STRIDE * 2;
-constexpr int BWDG_LDS_BYTES = GRAD_LDS_BYTES > MAIN_LDS_BYTES ? GRAD_LDS_BYTES : MAIN_LDS_BYTES;
+constexpr int BWDG_LDS_BYTES = GRAD_LDS_BYTES > dma::LDS_BYTES ? GRAD_LDS_BYTES : dma::LDS_BYTES;
 
 template <bool TAIL>
 __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArgs& a, int v0,
@@ -532,27 +535,27 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArg
   }
 }
 
-__global__ __launch_bounds__(NTHREADS, 1) void k_grad(GradArgs a) {
+__global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_grad(GradArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[BWDG_LDS_BYTES / 2];
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int vt = tile / a.ntb, tb = tile % a.ntb;
+  int vt, tb;
+  vocab_token_tile(xcd_remap(blockIdx.x, gridDim.x), a.nvt, a.ntb, vt, tb);
   const int Ts = *a.count;
   const int j0 = tb * BN, v0 = vt * BM;
   if (j0 >= Ts) return;
-  const int t = threadIdx.x, c = t & 7, r0 = t >> 3;
-  LdK la, lb;
+  dma::Loader la, lb;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int v = v0 + r0 + 32 * i;
+  for (int u = 0; u < 4; ++u) {
+    const int r = dma::Loader::row_of(u), c = dma::Loader::chunk_of(u);
+    int v = v0 + r;
     v = v < a.n_real ? v : (int)a.n_real - 1;
-    la.p[i] = a.W + (int64_t)v * a.ldw + c * 8;
-    int j = j0 + r0 + 32 * i;
+    la.p[u] = a.W + (int64_t)v * a.ldw + c * 8;
+    int j = j0 + r;
     j = j < Ts ? j : Ts - 1;
-    lb.p[i] = a.h + (int64_t)a.scored[j] * a.ldh + c * 8;
+    lb.p[u] = a.h + (int64_t)a.scored[j] * a.ldh + c * 8;
   }
   f32x16 acc[4][4];
   zero_acc(acc);
-  mainloop(la, lb, 0, a.H / BK, smem, acc);
+  dma::mainloop(la, lb, 0, a.H / dma::BKD, smem, acc);
   if (v0 + BM > a.n_real)
     grad_epilogue<true>(acc, a, v0, j0, Ts, smem);
   else
@@ -571,7 +574,7 @@ struct WRows {
 };
 
 // dhidden partials: P[split][j][n] = sum over the split's K range of G[j, k] W[k, n].
-__global__ __launch_bounds__(NTHREADS, 1) void k_dh(DhArgs a) {
+__global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dh(DhArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[MAIN_LDS_BYTES / 2];
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   // Logical order: split, then N tile, then M tile fastest.
@@ -645,7 +648,7 @@ struct GRows {
 };
 
 // dweight[v, n] += sum_j G[j, v] hg[j, n] over the scored rows j in order.
-__global__ __launch_bounds__(NTHREADS, 1) void k_dw(DwArgs a) {
+__global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dw(DwArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[MAIN_LDS_BYTES / 2];
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int nt = tile % a.ntn, mt = tile / a.ntn;

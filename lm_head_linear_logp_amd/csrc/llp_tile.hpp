@@ -58,6 +58,20 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return x * full + (x < rem ? x : rem) + i;
 }
 
+// Logical tile -> (vocabulary tile, token block) for the vocabulary x token grids. Tiles
+// run in groups of 8 vocabulary tiles x all token blocks, token block slowest within a group:
+// the 32 workgroups an XCD runs at once then cover 8 vocabulary tiles x 4 token blocks, whose
+// operands (8 weight + 4 hidden tiles, 24 MiB) are each fetched once into that XCD's L2 per
+// round. Bijective for any grid.
+constexpr int VOCAB_GROUP = 8;
+__device__ __forceinline__ void vocab_token_tile(int tile, int nvt, int ntb, int& vt, int& tb) {
+  const int grp = tile / (VOCAB_GROUP * ntb), gi = tile % (VOCAB_GROUP * ntb);
+  const int rest = nvt - grp * VOCAB_GROUP;
+  const int gsz = rest < VOCAB_GROUP ? rest : VOCAB_GROUP;
+  vt = grp * VOCAB_GROUP + gi % gsz;
+  tb = gi / gsz;
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -138,21 +152,31 @@ struct Frag {
   }
 };
 
+__device__ __forceinline__ void load_frag(const uint16_t* As, const uint16_t* Bs, const Frag& f,
+                                          int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = *reinterpret_cast<const bf16x8*>(As + f.aoff[i] + (((2 * kk) ^ f.at[i]) << 3));
+    b[i] = *reinterpret_cast<const bf16x8*>(Bs + f.boff[i] + (((2 * kk) ^ f.bt[i]) << 3));
+  }
+}
+
+// 4 K-substeps of 16; the operands of substep kk+1 are read while the 16 MFMAs of kk run.
 __device__ __forceinline__ void mma_stage(const uint16_t* As, const uint16_t* Bs,
                                           const Frag& f, f32x16 (&acc)[4][4]) {
+  bf16x8 a[2][4], b[2][4];
+  load_frag(As, Bs, f, 0, a[0], b[0]);
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) {
-    bf16x8 a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = *reinterpret_cast<const bf16x8*>(As + f.aoff[i] + (((2 * kk) ^ f.at[i]) << 3));
-      b[i] = *reinterpret_cast<const bf16x8*>(Bs + f.boff[i] + (((2 * kk) ^ f.bt[i]) << 3));
-    }
+    if (kk + 1 < BK / 16) load_frag(As, Bs, f, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+    // Keep the prefetch ahead of this substep's MFMAs (the scheduler would sink it).
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][mi], b[kk & 1][ni],
+                                                              acc[mi][ni], 0, 0, 0);
   }
 }
 
@@ -196,5 +220,172 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int ks0, int ks1, uint1
   mma_stage(last, last + STAGE_ELEMS, f, acc);
   __syncthreads();
 }
+
+// ------------------------------------------------------------------------------------
+// Deep DMA pipeline for operands that are K-contiguous in memory (the fused forward and the
+// gradient recompute). K step BKD = 32, NST = 4 LDS stages of 2 x 16 KiB; the direct
+// global->LDS loads (global_load_lds_dwordx4) of step s+3 are issued right after the barrier
+// that opens step s, so a load has three steps of MFMA work (3 x 1024 MFMA cycles) to land.
+// One instruction moves 64 lanes x 16 bytes into a contiguous 1 KiB LDS window in lane
+// order: 16 rows of 4 chunks. Wave w fills rows 64w .. 64w+63 of each operand with 4
+// instructions; lane i of instruction u lands in row 64w + 16u + i/4 at slot i%4 and so
+// fetches that row's logical chunk (i%4) ^ swz4(row). swz4 keeps 8 (and 16) consecutive rows
+// reading one logical chunk on distinct banks.
+// ------------------------------------------------------------------------------------
+namespace dma {
+
+constexpr int BKD = 32;
+constexpr int NST = 4;
+constexpr int STAGE = BM * BKD;  // bf16 elements per operand per stage
+constexpr int LDS_BYTES = NST * 2 * STAGE * 2;
+
+__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+struct Loader {
+  const uint16_t* p[4];  // per instruction: this lane's global address at K step 0
+
+  __device__ __forceinline__ static int row_of(int u) {
+    return 64 * (threadIdx.x >> 6) + 16 * u + ((threadIdx.x & 63) >> 2);
+  }
+  __device__ __forceinline__ static int chunk_of(int u) {
+    return (threadIdx.x & 3) ^ swz4(row_of(u));
+  }
+  // One DMA instruction (u = 0..3) of this wave for K step `kstep` into `stage`.
+  __device__ __forceinline__ void issue1(uint16_t* stage, int kstep, int u) const {
+    // The wave index is uniform: keep the LDS destination (M0) in scalar registers.
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(p[u] + kstep * BKD),
+        (__attribute__((address_space(3))) void*)(stage + (64 * w + 16 * u) * BKD), 16, 0, 0);
+  }
+  __device__ __forceinline__ void issue(uint16_t* stage, int kstep) const {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) issue1(stage, kstep, u);
+  }
+};
+
+struct Frag {
+  int aoff[4], at[4], boff[4], bt[4];
+  __device__ __forceinline__ void init(int wm, int wn, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ra = wm * 128 + i * 32 + (lane & 31);
+      const int rb = wn * 128 + i * 32 + (lane & 31);
+      aoff[i] = ra * BKD;
+      at[i] = (lane >> 5) ^ swz4(ra);
+      boff[i] = rb * BKD;
+      bt[i] = (lane >> 5) ^ swz4(rb);
+    }
+  }
+};
+
+__device__ __forceinline__ void load_frag(const uint16_t* As, const uint16_t* Bs, const Frag& f,
+                                          int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = *reinterpret_cast<const bf16x8*>(As + f.aoff[i] + (((2 * kk) ^ f.at[i]) << 3));
+    b[i] = *reinterpret_cast<const bf16x8*>(Bs + f.boff[i] + (((2 * kk) ^ f.bt[i]) << 3));
+  }
+}
+
+// MFMAs number lo..hi-1 of one 16-deep substep, in (mi, ni) row-major order.
+template <int LO, int HI>
+__device__ __forceinline__ void mfmas(const bf16x8 (&a)[4], const bf16x8 (&b)[4],
+                                      f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int k = LO; k < HI; ++k)
+    acc[k >> 2][k & 3] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k >> 2], b[k & 3], acc[k >> 2][k & 3], 0, 0, 0);
+}
+
+// Wait until at most n of this wave's vector-memory instructions are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt at maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that orders LDS only: this wave's LDS reads have returned (lgkmcnt 0)
+// before any wave passes. __syncthreads() would also drain every vector-memory load,
+// including the DMA loads still in flight for later steps. The memory clobber keeps the
+// compiler from moving memory accesses across it; DMA completion is waited for explicitly.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// sched_group_barrier masks (LLVM AMDGPU): MFMA, VMEM read, DS read.
+constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
+
+// acc += A[M-tile, K-steps ks0..ks1) . B[N-tile, same]^T in ascending K order.
+// Each K step s has two 16-deep substeps (kk0, kk1) in separate fragment registers and two
+// branch-free regions, interleaved one memory instruction per MFMA:
+//   A: [MFMA kk0, read kk1] x 8, MFMA kk0 x 8
+//   -- wait for step s+1, barrier (step s's stage is released) --
+//   B: [MFMA kk1, DMA of step s+4 into the released stage] x 8,
+//      [MFMA kk1, read kk0 of step s+1] x 8
+// DMA steps past the end are clamped to the last step (an in-bounds reload into a stage that
+// is never read again), so every iteration has the same shape and the same vmcnt wait: after
+// iteration s-1 the DMAs of steps s+1..s+3 (24 instructions per wave) are outstanding, and
+// step s+1 has landed once at most 16 remain. All DMA is drained before returning.
+__device__ __forceinline__ void mainloop(const Loader& la, const Loader& lb, int ks0, int ks1,
+                                         uint16_t* smem, f32x16 (&acc)[4][4]) {
+  const int n = ks1 - ks0;
+  if (n <= 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  Frag f;
+  f.init(wave & 1, wave >> 1, lane);
+#pragma unroll
+  for (int s = 0; s < NST; ++s) {
+    const int k = ks0 + (s < n ? s : n - 1);
+    la.issue(smem + s * 2 * STAGE, k);
+    lb.issue(smem + s * 2 * STAGE + STAGE, k);
+  }
+  wait_vmem_le<24>();
+  lds_barrier();
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  load_frag(smem, smem + STAGE, f, 0, a0, b0);
+  for (int s = 0; s < n; ++s) {
+    const uint16_t* cur = smem + (s % NST) * 2 * STAGE;
+    uint16_t* freed = smem + (s % NST) * 2 * STAGE;
+    const uint16_t* nx = smem + ((s + 1) % NST) * 2 * STAGE;
+    const int kd = ks0 + (s + NST < n ? s + NST : n - 1);
+    // Region A.
+    mfmas<0, 16>(a0, b0, acc);
+    load_frag(cur, cur + STAGE, f, 1, a1, b1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmem_le<16>();
+    lds_barrier();
+    // Region B.
+    mfmas<0, 16>(a1, b1, acc);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      la.issue1(freed, kd, u);
+      lb.issue1(freed + STAGE, kd, u);
+    }
+    load_frag(nx, nx + STAGE, f, 0, a0, b0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 1);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_vmem_le<0>();
+  __syncthreads();
+}
+
+}  // namespace dma
 
 }  // namespace llp
