@@ -107,7 +107,7 @@ llp_status check_request(const llp_request* req) {
 
 // Workspace regions (byte offsets, each 256-byte aligned).
 struct Ws {
-  size_t count, scored, pos, tloc, tz, pm, ps, pq, G, hg, P, total;
+  size_t count, scored, pos, tloc, tz, pm, ps, pq, G, Gt, hgT, WT, P, total;
   int64_t T_cap, nvt, ldg;
 };
 
@@ -132,8 +132,10 @@ Ws ws_layout(int64_t T, int64_t n_real, int64_t H, int op) {
     w.ps = take((size_t)(w.nvt * w.T_cap) * 4);
     w.pq = take((size_t)(w.nvt * w.T_cap) * 4);
   } else {
-    w.G = take((size_t)w.T_cap * (size_t)w.ldg * 2);
-    w.hg = take((size_t)w.T_cap * (size_t)H * 2);
+    w.G = take((size_t)w.T_cap * (size_t)w.ldg * 2);    // G[j][v]
+    w.Gt = take((size_t)w.ldg * (size_t)w.T_cap * 2);   // G^T[v][j]
+    w.hgT = take((size_t)H * (size_t)w.T_cap * 2);      // scored hidden rows, transposed
+    w.WT = take((size_t)H * (size_t)w.ldg * 2);         // weight, transposed
     w.P = take((size_t)DH_SPLITS * (size_t)w.T_cap * (size_t)H * 4);
   }
   w.total = off;
@@ -203,7 +205,8 @@ LLP_API llp_status llp_open(int32_t device, llp_info* info) {
     snprintf(info->version, sizeof(info->version), "%s", LLP_VERSION);
     snprintf(info->arch, sizeof(info->arch), "%.31s", prop.gcnArchName);
     snprintf(info->route, sizeof(info->route),
-             "hip-gfx950 mfma32x32x16bf16 tile256x256x64 w4 lds2stage xcd8 dhsplit%d", DH_SPLITS);
+             "hip-gfx950 mfma32x32x16bf16 tile256x256 bk32 w4 lds-dma4 xcd8 vgroup8 dhsplit%d",
+             DH_SPLITS);
     info->max_replay_ids = LLP_MAX_REPLAY_IDS;
     info->num_cus = prop.multiProcessorCount;
     info->device = device;
@@ -400,8 +403,32 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
 
   const int ntb = (int)(w.T_cap / TILE);
   uint16_t* G = at<uint16_t>(workspace, w.G);
+  uint16_t* Gt = at<uint16_t>(workspace, w.Gt);
+  uint16_t* hgT = at<uint16_t>(workspace, w.hgT);
+  uint16_t* WT = at<uint16_t>(workspace, w.WT);
   float* P = at<float>(workspace, w.P);
   if (n_real > 0) {
+    // K-contiguous operand copies for the two products: the scored hidden rows transposed
+    // (hgT[h][j], zero past the count) and the weight transposed (WT[h][v], zero past the
+    // shard's real columns).
+    TransposeArgs th{};
+    th.in = static_cast<const uint16_t*>(req->proj.hidden);
+    th.ldi = req->proj.hidden_stride;
+    th.idx = la.scored;
+    th.count = la.count;
+    th.cols = (int32_t)H;
+    th.out = hgT;
+    th.ldo = w.T_cap;
+    LLP_HIP(launch_transpose(th, w.T_cap, s), "transpose kernel launch");
+    TransposeArgs tw{};
+    tw.in = static_cast<const uint16_t*>(req->proj.weight);
+    tw.ldi = req->proj.weight_stride;
+    tw.nvalid = n_real;
+    tw.cols = (int32_t)H;
+    tw.out = WT;
+    tw.ldo = w.ldg;
+    LLP_HIP(launch_transpose(tw, w.ldg, s), "transpose kernel launch");
+
     GradArgs ga{};
     ga.W = static_cast<const uint16_t*>(req->proj.weight);
     ga.ldw = req->proj.weight_stride;
@@ -423,37 +450,30 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
     ga.ent = in->entropy;
     ga.G = G;
     ga.ldg = w.ldg;
+    ga.Gt = Gt;
+    ga.ldgt = w.T_cap;
     LLP_HIP(launch_grad(ga, s), "gradient kernel launch");
 
     DhArgs da{};
     da.G = G;
     da.ldg = w.ldg;
-    da.W = ga.W;
-    da.ldw = ga.ldw;
+    da.WT = WT;
+    da.ldwt = w.ldg;
     da.n_real = n_real;
     da.H = (int32_t)H;
     da.ntm = ntb;
     da.ntn = (int32_t)((H + TILE - 1) / TILE);
     da.nsplit = DH_SPLITS;
-    da.nks = (int32_t)((n_real + 63) / 64);
+    da.nks = (int32_t)((n_real + 31) / 32);
     da.count = la.count;
     da.P = P;
     da.pstride = w.T_cap;
     LLP_HIP(launch_dh(da, s), "dhidden kernel launch");
 
-    GatherArgs gg{};
-    gg.h = ga.h;
-    gg.ldh = ga.ldh;
-    gg.H = (int32_t)H;
-    gg.count = la.count;
-    gg.scored = la.scored;
-    gg.hg = at<uint16_t>(workspace, w.hg);
-    LLP_HIP(launch_gather(gg, w.T_cap, s), "gather kernel launch");
-
     DwArgs wa{};
-    wa.G = G;
-    wa.ldg = w.ldg;
-    wa.hg = gg.hg;
+    wa.Gt = Gt;
+    wa.hgT = hgT;
+    wa.ldk = w.T_cap;
     wa.H = (int32_t)H;
     wa.ntm = (int32_t)w.nvt;
     wa.ntn = da.ntn;

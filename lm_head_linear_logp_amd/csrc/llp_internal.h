@@ -125,13 +125,15 @@ struct GradArgs {
   const float* ent;
   uint16_t* G;
   int64_t ldg;
+  uint16_t* Gt;
+  int64_t ldgt;
 };
 
 struct DhArgs {
   const uint16_t* G;
   int64_t ldg;
-  const uint16_t* W;
-  int64_t ldw;
+  const uint16_t* WT;
+  int64_t ldwt;
   int64_t n_real;
   int32_t H;
   int32_t ntm, ntn, nsplit, nks;
@@ -152,9 +154,9 @@ struct DhReduceArgs {
 };
 
 struct DwArgs {
-  const uint16_t* G;
-  int64_t ldg;
-  const uint16_t* hg;
+  const uint16_t* Gt;
+  const uint16_t* hgT;
+  int64_t ldk;  // row stride of Gt and hgT (the scored-row capacity)
   int32_t H;
   int32_t ntm, ntn;
   int64_t n_real;
@@ -163,13 +165,15 @@ struct DwArgs {
   int64_t lddw;
 };
 
-struct GatherArgs {
-  const uint16_t* h;
-  int64_t ldh;
-  int32_t H;
-  const int32_t* count;
-  const int32_t* scored;
-  uint16_t* hg;
+struct TransposeArgs {
+  const uint16_t* in;
+  int64_t ldi;
+  const int32_t* idx;    // row gather list or null
+  const int32_t* count;  // number of valid rows on the device, or null (use nvalid)
+  int64_t nvalid;
+  int32_t cols;          // columns of `in` read (multiple of 64)
+  uint16_t* out;
+  int64_t ldo;
 };
 
 struct DbArgs {
@@ -189,7 +193,7 @@ hipError_t launch_grad(const GradArgs& a, hipStream_t s);
 hipError_t launch_dh(const DhArgs& a, hipStream_t s);
 hipError_t launch_dh_reduce(const DhReduceArgs& a, hipStream_t s);
 hipError_t launch_dw(const DwArgs& a, hipStream_t s);
-hipError_t launch_gather(const GatherArgs& a, int64_t T_cap, hipStream_t s);
+hipError_t launch_transpose(const TransposeArgs& a, int64_t rows, hipStream_t s);
 hipError_t launch_dbias(const DbArgs& a, hipStream_t s);
 hipError_t probe_kernels();
 

@@ -484,6 +484,7 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArg
     de[ni] = a.dent ? a.dent[row] : 0.f;
     ez[ni] = a.dent ? lse[ni] - a.ent[row] : 0.f;
     tl[ni] = a.tloc[jj] - vbase;
+    if (j >= Ts) dl[ni] = de[ni] = 0.f;  // rows past the count: exact zeros in G and Gt
   }
   // Stage the bf16 tile as Gs[token][vocab] in LDS, then write full rows.
   __syncthreads();
@@ -508,10 +509,12 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArg
         for (int u = 0; u < 4; ++u) {
           const int r = rg * 4 + u;
           const int vl = mi * 32 + mfma_row(r, lane);
-          const float z = a.bias != nullptr ? (acc[mi][ni][r] + b[r]) * a.c1 : acc[mi][ni][r] * a.c1;
+          const float av = acc_read(acc[mi][ni][r]);
+          const float z = a.bias != nullptr ? (av + b[r]) * a.c1 : av * a.c1;
           const float p = __builtin_amdgcn_exp2f((z - lse[ni]) * kLog2e);
           float g = dl[ni] * ((vl == tl[ni] ? 1.f : 0.f) - p);
           if (a.dent) g -= de[ni] * p * (z - ez[ni]);
+          if (dl[ni] == 0.f && de[ni] == 0.f) g = 0.f;  // no gradient flows: exact 0
           g *= a.c1;
           if (TAIL && vbase + vl >= a.n_real) g = 0.f;
           const uint32_t hb = f32_to_bf16_rne(g);
@@ -526,12 +529,30 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArg
     }
   }
   __syncthreads();
+  // G[j][v0 .. v0+255] for the scored rows of the tile (K = vocabulary for dhidden).
   for (int idx = threadIdx.x; idx < BN * (BM / 8); idx += NTHREADS) {
     const int tn = idx >> 5, c = idx & 31;
     const int j = j0 + tn;
     if (j < Ts)
       *reinterpret_cast<u32x4*>(a.G + (int64_t)j * a.ldg + v0 + c * 8) =
           *reinterpret_cast<const u32x4*>(smem + tn * GT_STRIDE + c * 8);
+  }
+  // Gt[v][j0 .. j0+255] (K = scored row for dweight), zeros past the count: wave w writes
+  // the 64 columns 64w .. 64w+63 of vocabulary rows lane + 64c, one 128-byte line per lane.
+#pragma unroll 1
+  for (int c = 0; c < 4; ++c) {
+    const int vl = lane + 64 * c;
+    uint32_t pk[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const uint32_t lo = smem[(64 * wave + 2 * e) * GT_STRIDE + vl];
+      const uint32_t hi = smem[(64 * wave + 2 * e + 1) * GT_STRIDE + vl];
+      pk[e] = lo | (hi << 16);
+    }
+    uint16_t* dst = a.Gt + (int64_t)(v0 + vl) * a.ldgt + j0 + 64 * wave;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      reinterpret_cast<u32x4*>(dst)[q] = u32x4{pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]};
   }
 }
 
@@ -562,41 +583,33 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
     grad_epilogue<false>(acc, a, v0, j0, Ts, smem);
 }
 
-// Rows of the weight as the K operand of dhidden = G W: W[k, n0 + 8 mb .. +7].
-struct WRows {
-  const uint16_t* W;
-  int64_t ldw;
-  int n_real;
-  int col;
-  __device__ __forceinline__ const uint16_t* operator()(int k) const {
-    return k < n_real ? W + (int64_t)k * ldw + col : nullptr;
-  }
-};
-
-// dhidden partials: P[split][j][n] = sum over the split's K range of G[j, k] W[k, n].
+// dhidden partials: P[split][j][n] = sum over the split's K range of G[j, k] WT[n, k]
+// (K = local vocabulary column; WT is the weight transposed, zero past the real columns).
+// Tiles: grouped like the vocabulary x token grids with M = scored-row tiles.
 __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dh(DhArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[MAIN_LDS_BYTES / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  // Logical order: split, then N tile, then M tile fastest.
-  const int mt = tile % a.ntm;
-  const int nt = (tile / a.ntm) % a.ntn;
-  const int sp = tile / (a.ntm * a.ntn);
+  const int per = a.ntm * a.ntn;
+  const int sp = tile / per;
+  int mt, nt;
+  vocab_token_tile(tile % per, a.ntm, a.ntn, mt, nt);
   const int Ts = *a.count;
   const int j0 = mt * BM, n0 = nt * BN;
   if (j0 >= Ts) return;
-  const int t = threadIdx.x, c = t & 7, r0 = t >> 3;
-  LdK la;
+  dma::Loader la, lb;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) la.p[i] = a.G + (int64_t)(j0 + r0 + 32 * i) * a.ldg + c * 8;
-  int col = n0 + (t & 31) * 8;
-  col = col <= a.H - 8 ? col : a.H - 8;
-  LdMN<WRows> lb{WRows{a.W, a.ldw, (int)a.n_real, col}};
+  for (int u = 0; u < 4; ++u) {
+    const int r = dma::Loader::row_of(u), c = dma::Loader::chunk_of(u);
+    la.p[u] = a.G + (int64_t)(j0 + r) * a.ldg + c * 8;
+    const int n = n0 + r < a.H ? n0 + r : a.H - 1;
+    lb.p[u] = a.WT + (int64_t)n * a.ldwt + c * 8;
+  }
   const int ks0 = (int)((int64_t)a.nks * sp / a.nsplit);
   const int ks1 = (int)((int64_t)a.nks * (sp + 1) / a.nsplit);
   f32x16 acc[4][4];
   zero_acc(acc);
-  mainloop(la, lb, ks0, ks1, smem, acc);
-  const int lane = t & 63, wave = t >> 6, wm = wave & 1, wn = wave >> 1;
+  dma::mainloop(la, lb, ks0, ks1, smem, acc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   float* P = a.P + (int64_t)sp * a.pstride * a.H;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
@@ -636,59 +649,99 @@ __global__ __launch_bounds__(256) void k_dh_reduce(DhReduceArgs a) {
   *reinterpret_cast<u32x4*>(a.dH + t * a.ldd + n) = u32x4{pk[0], pk[1], pk[2], pk[3]};
 }
 
-// Rows of G (K = scored token) restricted to 8 vocabulary columns, zero past the count.
-struct GRows {
-  const uint16_t* G;
-  int64_t ldg;
-  int Ts;
-  int col;
-  __device__ __forceinline__ const uint16_t* operator()(int k) const {
-    return k < Ts ? G + (int64_t)k * ldg + col : nullptr;
-  }
-};
-
-// dweight[v, n] += sum_j G[j, v] hg[j, n] over the scored rows j in order.
+// dweight[v, n] += sum_j Gt[v, j] hgT[n, j] over the scored rows j in ascending order
+// (Gt and hgT are zero past the count, so whole 32-row K steps can be used).
 __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dw(DwArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[MAIN_LDS_BYTES / 2];
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int nt = tile % a.ntn, mt = tile / a.ntn;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
+  int mt, nt;
+  vocab_token_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntm, a.ntn, mt, nt);
   const int Ts = *a.count;
+  if (Ts <= 0) return;
   const int m0 = mt * BM, n0 = nt * BN;
-  const int t = threadIdx.x;
-  int ncol = n0 + (t & 31) * 8;
-  ncol = ncol <= a.H - 8 ? ncol : a.H - 8;
-  LdMN<GRows> la{GRows{a.G, a.ldg, Ts, m0 + (t & 31) * 8}};
-  LdMN<GRows> lb{GRows{a.hg, (int64_t)a.H, Ts, ncol}};
+  dma::Loader la, lb;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = dma::Loader::row_of(u), c = dma::Loader::chunk_of(u);
+    la.p[u] = a.Gt + (int64_t)(m0 + r) * a.ldk + c * 8;
+    const int n = n0 + r < a.H ? n0 + r : a.H - 1;
+    lb.p[u] = a.hgT + (int64_t)n * a.ldk + c * 8;
+  }
   f32x16 acc[4][4];
   zero_acc(acc);
-  mainloop(la, lb, 0, (Ts + BK - 1) / BK, smem, acc);
-  const int lane = t & 63, wave = t >> 6, wm = wave & 1, wn = wave >> 1;
+  dma::mainloop(la, lb, 0, (Ts + dma::BKD - 1) / dma::BKD, smem, acc);
+  // dweight += acc, 64 values per row block mi; the loads of block mi+1 are issued before the
+  // adds and stores of block mi so that HBM latency is paid about once per tile.
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  const bool full = m0 + BM <= a.n_real && n0 + BN <= a.H;
+  float cur[4][16], nxt[4][16];
+  auto ptr = [&](int mi, int ni, int r) {
+    const int v = m0 + wm * 128 + mi * 32 + mfma_row(r, lane);
+    const int n = n0 + wn * 128 + ni * 32 + (lane & 31);
+    return a.dW + (int64_t)v * a.lddw + n;
+  };
+  auto ok = [&](int mi, int ni, int r) {
+    const int v = m0 + wm * 128 + mi * 32 + mfma_row(r, lane);
+    const int n = n0 + wn * 128 + ni * 32 + (lane & 31);
+    return full || (v < a.n_real && n < a.H);
+  };
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int n = n0 + wn * 128 + ni * 32 + (lane & 31);
+    for (int r = 0; r < 16; ++r) cur[ni][r] = ok(0, ni, r) ? *ptr(0, ni, r) : 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = m0 + wm * 128 + mi * 32 + mfma_row(r, lane);
-        if (v < a.n_real && n < a.H) {
-          float* d = a.dW + (int64_t)v * a.lddw + n;
-          *d = *d + acc[mi][ni][r];
-        }
-      }
+  for (int mi = 0; mi < 4; ++mi) {
+    if (mi + 1 < 4) {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) nxt[ni][r] = ok(mi + 1, ni, r) ? *ptr(mi + 1, ni, r) : 0.f;
     }
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (ok(mi, ni, r)) *ptr(mi, ni, r) = cur[ni][r] + acc_read(acc[mi][ni][r]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cur[ni][r] = nxt[ni][r];
+  }
 }
 
-// hg[j] = hidden[scored[j]] (compact copy of the scored rows for the dweight product).
-__global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
-  const int Ts = *a.count;
-  const int64_t cpr = a.H / 8;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)Ts * cpr) return;
-  const int64_t j = idx / cpr;
-  const int n = (int)(idx % cpr) * 8;
-  *reinterpret_cast<u32x4*>(a.hg + j * a.H + n) =
-      *reinterpret_cast<const u32x4*>(a.h + (int64_t)a.scored[j] * a.ldh + n);
+// out[c][r] = in[row(r)][c] for r < nvalid (zero for nvalid <= r < the grid's rows), 64 x 64
+// bf16 tiles through LDS. row(r) = idx[r] when an index list is given, else r; nvalid is
+// *count when given. Makes hgT (gathered hidden rows, transposed) and WT (weight transposed).
+__global__ __launch_bounds__(256) void k_transpose(TransposeArgs a) {
+  __shared__ uint16_t t[64][66];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int nvalid = a.count ? *a.count : (int)a.nvalid;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int r = q >> 3, cc = q & 7;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r0 + r < nvalid) {
+      const int64_t row = a.idx ? a.idx[r0 + r] : r0 + r;
+      v = *reinterpret_cast<const u32x4*>(a.in + row * a.ldi + c0 + cc * 8);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      t[r][cc * 8 + 2 * e] = (uint16_t)(v[e] & 0xFFFFu);
+      t[r][cc * 8 + 2 * e + 1] = (uint16_t)(v[e] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int c = q >> 3, rc = q & 7;
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (uint32_t)t[rc * 8 + 2 * e][c] | ((uint32_t)t[rc * 8 + 2 * e + 1][c] << 16);
+    *reinterpret_cast<u32x4*>(a.out + (int64_t)(c0 + c) * a.ldo + r0 + rc * 8) = o;
+  }
 }
 
 // dbias[v] += sum_j G[j, v] over scored rows in order.
@@ -754,9 +807,10 @@ hipError_t launch_dw(const DwArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const GatherArgs& a, int64_t T_cap, hipStream_t s) {
-  const int64_t n = T_cap * (a.H / 8);
-  if (n > 0) hipLaunchKernelGGL(k_gather, dim3(ceil_div64(n, 256)), dim3(256), 0, s, a);
+hipError_t launch_transpose(const TransposeArgs& a, int64_t rows, hipStream_t s) {
+  if (rows > 0 && a.cols > 0)
+    hipLaunchKernelGGL(k_transpose, dim3((unsigned)(rows / 64), (unsigned)(a.cols / 64)), dim3(256),
+                       0, s, a);
   return hipGetLastError();
 }
 
