@@ -62,7 +62,45 @@ def measured_traffic():
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(rows: int = 192) -> dict:
+def ingest_pmc(fetch_csv: str, write_csv: str) -> None:
+    """Write profiles/traffic_fwd_kernel.json from two rocprofv3 --pmc counter CSVs (one pass
+    with FETCH_SIZE, one with WRITE_SIZE, both of `bench.py --copy-calibration`). Each counter
+    (KiB per dispatch) is scaled by the ratio of the known bytes of the 1 GiB device copy to
+    what the same counter reads for that copy."""
+    import csv
+
+    def per_dispatch(path, counter):
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(open(path))
+                if r["Counter_Name"] == counter]
+
+    fd, wd = per_dispatch(fetch_csv, "FETCH_SIZE"), per_dispatch(write_csv, "WRITE_SIZE")
+    fwd = next(k for k, _ in fd if "k_fwd" in k)
+
+    def mean(ds, name):
+        v = [x for k, x in ds if k == name]
+        return sum(v) / len(v)
+
+    # The calibration copy is the largest copy dispatch (other copies move a few KiB).
+    copy = "__amd_rocclr_copyBuffer"
+    f = {fwd: mean(fd, fwd), copy: max(x for k, x in fd if k == copy)}
+    w = {fwd: mean(wd, fwd), copy: max(x for k, x in wd if k == copy)}
+    gib_kib = (1 << 30) / 1024.0
+    fs, ws = gib_kib / f[copy], gib_kib / w[copy]
+    out = {"kernel": fwd, "kernel_source_hash": kernel_source_hash(),
+           "fetch_kib_per_dispatch": f[fwd], "write_kib_per_dispatch": w[fwd],
+           "copy_kernel": copy, "copy_fetch_kib": f[copy], "copy_write_kib": w[copy],
+           "fetch_scale": fs, "write_scale": ws,
+           "bytes_per_launch": (f[fwd] * fs + w[fwd] * ws) * 1024.0,
+           "algorithmic_bytes_per_launch": float(2 * (VR * H + T * H) + T * 64),
+           "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
+                      "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration"}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def cpu_baseline(rows: int = 1536) -> dict:
     """The fp64 oracle (as it stands) on `rows` rows of the same workload: forward + backward
     of each row, timed on this host's cores; scaled to scored tokens/s."""
     import oracle
@@ -94,8 +132,15 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=192)
+    ap.add_argument("--cpu-rows", type=int, default=1536)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device copy before the warm-up (counter calibration)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the forward kernel's measured HBM traffic and exit")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the one-GPU hot path only; runs on more than one GPU are not "
               "part of this build (see the sharding notes in DESIGN.md).", file=sys.stderr)
@@ -153,6 +198,12 @@ def main():
         if e: e[4].record(stream)
         return e
 
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step(False)
