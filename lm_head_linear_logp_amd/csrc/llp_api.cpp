@@ -464,7 +464,7 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
     da.ntm = ntb;
     da.ntn = (int32_t)((H + TILE - 1) / TILE);
     da.nsplit = DH_SPLITS;
-    da.nks = (int32_t)((n_real + 31) / 32);
+    da.nks = (int32_t)((n_real + KSTEP - 1) / KSTEP);
     da.count = la.count;
     da.P = P;
     da.pstride = w.T_cap;

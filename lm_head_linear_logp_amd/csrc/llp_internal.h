@@ -13,6 +13,7 @@ namespace llp {
 // row's summation order never depends on the batch.
 constexpr int DH_SPLITS = 4;
 constexpr int TILE = 256;  // BM = BN of every GEMM tile
+constexpr int KSTEP = 64;  // K depth of one pipelined GEMM step
 
 struct LayoutArgs {
   int64_t T;

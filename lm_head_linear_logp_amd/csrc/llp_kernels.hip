@@ -212,6 +212,7 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const Fw
 
 // The epilogue reuses the pipeline's LDS for 6 x 256 fp32 partials.
 static_assert(6 * 256 * 4 <= dma::LDS_BYTES, "forward epilogue LDS");
+static_assert(dma::BKD == KSTEP, "K step shared with the host");
 
 __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   if (j0 >= Ts) return;
   dma::Loader la, lb;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < dma::NI; ++u) {
     const int r = dma::Loader::row_of(u), c = dma::Loader::chunk_of(u);
     int v = v0 + r;
     v = v < a.n_real ? v : (int)a.n_real - 1;
@@ -565,7 +566,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   if (j0 >= Ts) return;
   dma::Loader la, lb;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < dma::NI; ++u) {
     const int r = dma::Loader::row_of(u), c = dma::Loader::chunk_of(u);
     int v = v0 + r;
     v = v < a.n_real ? v : (int)a.n_real - 1;
@@ -598,7 +599,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   if (j0 >= Ts) return;
   dma::Loader la, lb;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < dma::NI; ++u) {
     const int r = dma::Loader::row_of(u), c = dma::Loader::chunk_of(u);
     la.p[u] = a.G + (int64_t)(j0 + r) * a.ldg + c * 8;
     const int n = n0 + r < a.H ? n0 + r : a.H - 1;
@@ -650,7 +651,7 @@ __global__ __launch_bounds__(256) void k_dh_reduce(DhReduceArgs a) {
 }
 
 // dweight[v, n] += sum_j Gt[v, j] hgT[n, j] over the scored rows j in ascending order
-// (Gt and hgT are zero past the count, so whole 32-row K steps can be used).
+// (Gt and hgT are zero past the count up to the token tile, so whole K steps can be used).
 __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dw(DwArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
   int mt, nt;
@@ -660,7 +661,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int m0 = mt * BM, n0 = nt * BN;
   dma::Loader la, lb;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < dma::NI; ++u) {
     const int r = dma::Loader::row_of(u), c = dma::Loader::chunk_of(u);
     la.p[u] = a.Gt + (int64_t)(m0 + r) * a.ldk + c * 8;
     const int n = n0 + r < a.H ? n0 + r : a.H - 1;

@@ -85,45 +85,45 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
 }
 
 // ------------------------------------------------------------------------------------
-// Deep DMA pipeline for operands that are K-contiguous in memory (the fused forward and the
-// gradient recompute). K step BKD = 32, NST = 4 LDS stages of 2 x 16 KiB; the direct
-// global->LDS loads (global_load_lds_dwordx4) of step s+3 are issued right after the barrier
-// that opens step s, so a load has three steps of MFMA work (3 x 1024 MFMA cycles) to land.
-// One instruction moves 64 lanes x 16 bytes into a contiguous 1 KiB LDS window in lane
-// order: 16 rows of 4 chunks. Wave w fills rows 64w .. 64w+63 of each operand with 4
-// instructions; lane i of instruction u lands in row 64w + 16u + i/4 at slot i%4 and so
-// fetches that row's logical chunk (i%4) ^ swz4(row). swz4 keeps 8 (and 16) consecutive rows
-// reading one logical chunk on distinct banks.
+// DMA pipeline for operands that are K-contiguous in memory. K step BKD = 64 (128 bytes per
+// row: one whole L2 line, so a load instruction's requests are full lines; with 64-byte row
+// pieces the L1's request rate, not bandwidth, caps the stream below what the MFMAs need).
+// NST = 2 LDS stages of 2 x 32 KiB. One instruction moves 64 lanes x 16 bytes into a
+// contiguous 1 KiB LDS window in lane order: 8 rows of 8 chunks. Wave w fills rows
+// 64w .. 64w+63 of each operand with 8 instructions; lane i of instruction u lands in row
+// 64w + 8u + i/8 at slot i%8 and so fetches that row's logical chunk (i%8) ^ swz8(row).
+// swz8 puts 8 (and 16) consecutive rows reading one logical chunk on distinct banks.
 // ------------------------------------------------------------------------------------
 namespace dma {
 
-constexpr int BKD = 32;
-constexpr int NST = 4;
+constexpr int BKD = 64;
+constexpr int NST = 2;
+constexpr int NI = 8;            // load instructions per wave per operand per step
 constexpr int STAGE = BM * BKD;  // bf16 elements per operand per stage
 constexpr int LDS_BYTES = NST * 2 * STAGE * 2;
 
-__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
 
 struct Loader {
-  const uint16_t* p[4];  // per instruction: this lane's global address at K step 0
+  const uint16_t* p[NI];  // per instruction: this lane's global address at K step 0
 
   __device__ __forceinline__ static int row_of(int u) {
-    return 64 * (threadIdx.x >> 6) + 16 * u + ((threadIdx.x & 63) >> 2);
+    return 64 * (threadIdx.x >> 6) + 8 * u + ((threadIdx.x & 63) >> 3);
   }
   __device__ __forceinline__ static int chunk_of(int u) {
-    return (threadIdx.x & 3) ^ swz4(row_of(u));
+    return (threadIdx.x & 7) ^ swz8(row_of(u));
   }
-  // One DMA instruction (u = 0..3) of this wave for K step `kstep` into `stage`.
+  // One DMA instruction (u = 0..NI-1) of this wave for K step `kstep` into `stage`.
   __device__ __forceinline__ void issue1(uint16_t* stage, int kstep, int u) const {
     // The wave index is uniform: keep the LDS destination (M0) in scalar registers.
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     __builtin_amdgcn_global_load_lds(
         (const void*)(p[u] + kstep * BKD),
-        (__attribute__((address_space(3))) void*)(stage + (64 * w + 16 * u) * BKD), 16, 0, 0);
+        (__attribute__((address_space(3))) void*)(stage + (64 * w + 8 * u) * BKD), 16, 0, 0);
   }
   __device__ __forceinline__ void issue(uint16_t* stage, int kstep) const {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) issue1(stage, kstep, u);
+    for (int u = 0; u < NI; ++u) issue1(stage, kstep, u);
   }
 };
 
@@ -135,13 +135,15 @@ struct Frag {
       const int ra = wm * 128 + i * 32 + (lane & 31);
       const int rb = wn * 128 + i * 32 + (lane & 31);
       aoff[i] = ra * BKD;
-      at[i] = (lane >> 5) ^ swz4(ra);
+      at[i] = (lane >> 5) ^ swz8(ra);
       boff[i] = rb * BKD;
-      bt[i] = (lane >> 5) ^ swz4(rb);
+      bt[i] = (lane >> 5) ^ swz8(rb);
     }
   }
 };
 
+// Fragments of 16-deep substep kk (0..3): lane l holds k = 16kk + 8(l/32) + 0..7, which is
+// logical chunk 2kk + l/32 = (2kk) ^ (l/32).
 __device__ __forceinline__ void load_frag(const uint16_t* As, const uint16_t* Bs, const Frag& f,
                                           int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
 #pragma unroll
@@ -180,70 +182,97 @@ __device__ __forceinline__ void lds_barrier() {
 // sched_group_barrier masks (LLVM AMDGPU): MFMA, VMEM read, DS read.
 constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
 
+// Issue DMA instructions LO..HI-1 of one K step (instruction i: operand i&1, slot i>>1).
+template <int LO, int HI>
+__device__ __forceinline__ void issue_range(const Loader& la, const Loader& lb, uint16_t* stage,
+                                            int kstep) {
+#pragma unroll
+  for (int i = LO; i < HI; ++i) {
+    if (i & 1) lb.issue1(stage + STAGE, kstep, i >> 1);
+    else la.issue1(stage, kstep, i >> 1);
+  }
+}
+
+// Schedule of one region: 16 MFMAs, the 8 fragment reads in the first half (one per MFMA) and
+// D DMA instructions spread evenly over the 16 MFMAs.
+template <int D, int I>
+__device__ __forceinline__ void region_slot() {
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+  if constexpr (I < 8) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+  constexpr int nv = ((I + 1) * D) / 16 - (I * D) / 16;
+  if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, nv, 0);
+  if constexpr (I + 1 < 16) region_slot<D, I + 1>();
+}
+
+// Memory instructions of one region in slot order (the compiler keeps LDS reads and DMA
+// writes in program order, so the source order is the issue order): slot I < 8 reads fragment
+// I/2 of A (I even) or B (I odd) for substep kk; DMA instructions QB + (I*D)/16 .. of step
+// `kstep` into `dst` follow in their slots.
+template <int D, int QB, int I>
+__device__ __forceinline__ void region_mem(const Loader& la, const Loader& lb, const uint16_t* st,
+                                           const Frag& f, int kk, bf16x8 (&na)[4],
+                                           bf16x8 (&nb)[4], uint16_t* dst, int kstep) {
+  if constexpr (I < 8) {
+    constexpr int i = I >> 1;
+    if constexpr (I & 1)
+      nb[i] = *reinterpret_cast<const bf16x8*>(st + STAGE + f.boff[i] + (((2 * kk) ^ f.bt[i]) << 3));
+    else
+      na[i] = *reinterpret_cast<const bf16x8*>(st + f.aoff[i] + (((2 * kk) ^ f.at[i]) << 3));
+  }
+  issue_range<QB + (I * D) / 16, QB + ((I + 1) * D) / 16>(la, lb, dst, kstep);
+  if constexpr (I + 1 < 16) region_mem<D, QB, I + 1>(la, lb, st, f, kk, na, nb, dst, kstep);
+}
+
+// One region: 16 MFMAs on (a, b); fragment reads of substep kk from stage `st` into (na, nb);
+// DMA instructions QB .. QB+D-1 of step `kstep` into stage `dst`.
+template <int D, int QB>
+__device__ __forceinline__ void region(const Loader& la, const Loader& lb, const bf16x8 (&a)[4],
+                                       const bf16x8 (&b)[4], const uint16_t* st, const Frag& f,
+                                       int kk, bf16x8 (&na)[4], bf16x8 (&nb)[4], uint16_t* dst,
+                                       int kstep, f32x16 (&acc)[4][4]) {
+  mfmas<0, 16>(a, b, acc);
+  region_mem<D, QB, 0>(la, lb, st, f, kk, na, nb, dst, kstep);
+  region_slot<D, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // acc += A[M-tile, K-steps ks0..ks1) . B[N-tile, same]^T in ascending K order.
-// Each K step s has two 16-deep substeps (kk0, kk1) in separate fragment registers and two
-// branch-free regions, interleaved one memory instruction per MFMA:
-//   A: [MFMA kk0, read kk1] x 8, MFMA kk0 x 8
-//   -- wait for step s+1, barrier (step s's stage is released) --
-//   B: [MFMA kk1, DMA of step s+4 into the released stage] x 8,
-//      [MFMA kk1, read kk0 of step s+1] x 8
-// DMA steps past the end are clamped to the last step (an in-bounds reload into a stage that
-// is never read again), so every iteration has the same shape and the same vmcnt wait: after
-// iteration s-1 the DMAs of steps s+1..s+3 (24 instructions per wave) are outstanding, and
-// step s+1 has landed once at most 16 remain. All DMA is drained before returning.
+// Step s (stage s%2) runs four 16-deep substeps in four branch-free regions; fragments
+// alternate between two register sets and each region reads the next substep's:
+//   R1:     MFMAs of kk0, reads of kk1, DMA of step s+1 (its last 8 loads)
+//   R2, R3: MFMAs of kk1, kk2, reads of kk2, kk3
+//   -- wait for step s+1's DMA, barrier (every wave is done reading stage s%2) --
+//   R4:     MFMAs of kk3, reads of kk0 of step s+1, DMA of step s+2 (its first 8 loads)
+// A step's 16 loads are split over two regions, one per two MFMAs: issued in one burst they
+// back up the address unit, and the in-order issue stalls the MFMAs queued behind them. DMA steps past
+// the end are clamped to the last step (an in-bounds reload into a stage that is never read
+// again), which keeps every iteration the same shape. All DMA is drained before returning.
 __device__ __forceinline__ void mainloop(const Loader& la, const Loader& lb, int ks0, int ks1,
                                          uint16_t* smem, f32x16 (&acc)[4][4]) {
+  constexpr int NQ = 2 * NI, Q4 = NI, Q1 = NI;  // loads per step: 8 in R4, 8 in R1
   const int n = ks1 - ks0;
   if (n <= 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   Frag f;
   f.init(wave & 1, wave >> 1, lane);
-#pragma unroll
-  for (int s = 0; s < NST; ++s) {
-    const int k = ks0 + (s < n ? s : n - 1);
-    la.issue(smem + s * 2 * STAGE, k);
-    lb.issue(smem + s * 2 * STAGE + STAGE, k);
-  }
-  wait_vmem_le<24>();
+  const int k1 = ks0 + (1 < n ? 1 : 0);
+  issue_range<0, NQ>(la, lb, smem, ks0);
+  issue_range<0, Q4>(la, lb, smem + 2 * STAGE, k1);
+  wait_vmem_le<Q4>();
   lds_barrier();
   bf16x8 a0[4], b0[4], a1[4], b1[4];
   load_frag(smem, smem + STAGE, f, 0, a0, b0);
   for (int s = 0; s < n; ++s) {
-    const uint16_t* cur = smem + (s % NST) * 2 * STAGE;
-    uint16_t* freed = smem + (s % NST) * 2 * STAGE;
-    const uint16_t* nx = smem + ((s + 1) % NST) * 2 * STAGE;
-    const int kd = ks0 + (s + NST < n ? s + NST : n - 1);
-    // Region A.
-    mfmas<0, 16>(a0, b0, acc);
-    load_frag(cur, cur + STAGE, f, 1, a1, b1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmem_le<16>();
+    uint16_t* cur = smem + (s & 1) * 2 * STAGE;
+    uint16_t* nx = smem + ((s + 1) & 1) * 2 * STAGE;
+    const int kn = ks0 + (s + 1 < n ? s + 1 : n - 1);
+    const int kd = ks0 + (s + 2 < n ? s + 2 : n - 1);
+    region<Q1, Q4>(la, lb, a0, b0, cur, f, 1, a1, b1, nx, kn, acc);
+    region<NQ - Q4 - Q1, Q4 + Q1>(la, lb, a1, b1, cur, f, 2, a0, b0, nx, kn, acc);
+    region<0, 0>(la, lb, a0, b0, cur, f, 3, a1, b1, nx, kn, acc);
+    wait_vmem_le<0>();
     lds_barrier();
-    // Region B.
-    mfmas<0, 16>(a1, b1, acc);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      la.issue1(freed, kd, u);
-      lb.issue1(freed + STAGE, kd, u);
-    }
-    load_frag(nx, nx + STAGE, f, 0, a0, b0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 1);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    region<Q4, 0>(la, lb, a1, b1, nx, f, 0, a0, b0, cur, kd, acc);
   }
   wait_vmem_le<0>();
   __syncthreads();
