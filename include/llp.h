@@ -97,7 +97,8 @@ typedef struct {
  *   weight  [local_size, H] bf16 -- this shard's rows of the LM-head weight, row stride
  *           weight_stride (elements, >= H, multiple of 8), 16-byte aligned base. Rows past the
  *           shard's real columns (padding) are never read into a result.
- *   bias    [local_size] of bias_dtype (LLP_DTYPE_BF16 or LLP_DTYPE_F32), or NULL.
+ *   bias    [local_size] of bias_dtype (LLP_DTYPE_BF16 or LLP_DTYPE_F32), or NULL; 16-byte
+ *           aligned base for F32, 8-byte for BF16.
  *   H must be a positive multiple of 64 (else LLP_ERR_UNSUPPORTED). */
 typedef struct {
   const void* hidden;

@@ -93,9 +93,12 @@ llp_status check_request(const llp_request* req) {
     LLP_CHECK(p.weight != nullptr, LLP_ERR_INVALID_ARGUMENT, "proj.weight is NULL");
     LLP_CHECK(aligned(p.weight, 16), LLP_ERR_INVALID_ARGUMENT, "proj.weight not 16-byte aligned");
   }
-  if (p.bias != nullptr)
+  if (p.bias != nullptr) {
     LLP_CHECK(p.bias_dtype == LLP_DTYPE_BF16 || p.bias_dtype == LLP_DTYPE_F32,
               LLP_ERR_INVALID_ARGUMENT, "bias_dtype %d is not BF16 or F32", p.bias_dtype);
+    LLP_CHECK(aligned(p.bias, p.bias_dtype == LLP_DTYPE_F32 ? 16 : 8), LLP_ERR_INVALID_ARGUMENT,
+              "proj.bias not %d-byte aligned", p.bias_dtype == LLP_DTYPE_F32 ? 16 : 8);
+  }
   LLP_CHECK(isfinite(req->temperature) && req->temperature > 0.f, LLP_ERR_INVALID_ARGUMENT,
             "temperature must be finite and > 0");
   LLP_CHECK((req->flags & ~uint32_t(LLP_FLAG_WANT_ENTROPY)) == 0, LLP_ERR_INVALID_ARGUMENT,

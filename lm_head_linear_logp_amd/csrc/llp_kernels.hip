@@ -87,51 +87,89 @@ __global__ __launch_bounds__(1024) void k_layout(LayoutArgs a) {
 // MFMA operand A = weight rows (vocabulary, M), B = hidden rows (tokens, N): each lane owns
 // one token column, so the per-row reductions run down its own registers first.
 // ------------------------------------------------------------------------------------
-template <bool TAIL>
-__device__ __forceinline__ void load_bias16(const void* bias, int bias_f32, int vb, int lane,
-                                            int64_t n_real, float (&b)[16]) {
+// Bias modes of the fused tiles: none, bf16 or fp32 vector (one instantiation each).
+constexpr int BIAS_NONE = 0, BIAS_BF16 = 1, BIAS_F32 = 2;
+
+// Bias of this lane's 16 accumulator rows of the 32-row block at vb: rows
+// vb + 8g + 4(lane/32) + 0..3 for g = 0..3 (mfma_row), i.e. four runs of four consecutive
+// rows, each read with one vector load (the bias is 16-byte aligned for fp32, 8-byte for
+// bf16). Rows at or past n_real (only in the shard's last tile) read as 0.
+template <int BMODE, bool TAIL>
+__device__ __forceinline__ void bias16(const void* bias, int vb, int lane, int64_t n_real,
+                                       float (&b)[16]) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int v = vb + mfma_row(r, lane);
-    b[r] = 0.f;
-    if (bias != nullptr && (!TAIL || v < n_real))
-      b[r] = bias_f32 ? reinterpret_cast<const float*>(bias)[v]
-                      : bf16_to_f32(reinterpret_cast<const uint16_t*>(bias)[v]);
+  for (int g = 0; g < 4; ++g) {
+    const int v = vb + 8 * g + 4 * (lane >> 5);
+    if constexpr (BMODE == BIAS_NONE) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) b[4 * g + u] = 0.f;
+    } else if (!TAIL || v + 3 < n_real) {
+      if constexpr (BMODE == BIAS_F32) {
+        const float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(bias) + v);
+        b[4 * g] = x.x;
+        b[4 * g + 1] = x.y;
+        b[4 * g + 2] = x.z;
+        b[4 * g + 3] = x.w;
+      } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(bias) + v);
+        b[4 * g] = __builtin_bit_cast(float, x.x << 16);
+        b[4 * g + 1] = __builtin_bit_cast(float, x.x & 0xFFFF0000u);
+        b[4 * g + 2] = __builtin_bit_cast(float, x.y << 16);
+        b[4 * g + 3] = __builtin_bit_cast(float, x.y & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float x = 0.f;
+        if (v + u < n_real)
+          x = BMODE == BIAS_F32 ? reinterpret_cast<const float*>(bias)[v + u]
+                                : bf16_to_f32(reinterpret_cast<const uint16_t*>(bias)[v + u]);
+        b[4 * g + u] = x;
+      }
+    }
   }
 }
 
-// z of accumulator element r, excluded columns -> -inf. Recomputed where needed so that the
-// 256 scaled logits of a lane are never stored alongside the accumulators.
-template <bool TAIL>
-__device__ __forceinline__ float zval(float acc, const float (&b)[16], int r, bool has_bias,
-                                      float c1, int vrow, int64_t n_real) {
-  const float z = has_bias ? (acc + b[r]) * c1 : acc * c1;
-  return (TAIL && vrow >= n_real) ? -INFINITY : z;
+// One bias value (the target column's), 0 without a bias.
+template <int BMODE>
+__device__ __forceinline__ float bias1(const void* bias, int v) {
+  if constexpr (BMODE == BIAS_F32) return reinterpret_cast<const float*>(bias)[v];
+  if constexpr (BMODE == BIAS_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(bias)[v]);
+  return 0.f;
 }
 
-template <bool TAIL>
+// x = acc (+ bias) of accumulator element r; z = x * c1.
+template <int BMODE>
+__device__ __forceinline__ float xval(float acc, const float (&b)[16], int r) {
+  if constexpr (BMODE == BIAS_NONE) return acc;
+  return acc + b[r];
+}
+
+template <bool TAIL, int BMODE>
 __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const FwdArgs& a, int vt,
                                              int v0, int j0, int Ts, uint16_t* smem) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int vbase = v0 + wm * 128;
-  const bool hb = a.bias != nullptr;
   float* red = reinterpret_cast<float*>(smem);  // [6][256]: max0 max1 s0 s1 q0 q1
-  // Pass 1: per-token max over this lane's 64 columns, then over the lane pair (l, l^32),
-  // then over the two waves holding the tile's two column halves.
+  // Pass 1: per-token max of x over this lane's 64 columns, the lane pair (l, l^32) and the two
+  // waves holding the tile's two column halves. z = x * c1 with c1 > 0 and rounding is
+  // monotonic, so fl(max x * c1) is the max of z.
   float mx[4];
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) mx[ni] = -INFINITY;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     float b[16];
-    load_bias16<TAIL>(a.bias, a.bias_f32, vbase + mi * 32, lane, a.n_real, b);
+    bias16<BMODE, TAIL>(a.bias, vbase + mi * 32, lane, a.n_real, b);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        mx[ni] = fmaxf(mx[ni], zval<TAIL>(acc[mi][ni][r], b, r, hb, a.c1,
-                                          vbase + mi * 32 + mfma_row(r, lane), a.n_real));
+      for (int r = 0; r < 16; ++r) {
+        float x = xval<BMODE>(acc[mi][ni][r], b, r);
+        if (TAIL && vbase + mi * 32 + mfma_row(r, lane) >= a.n_real) x = -INFINITY;
+        mx[ni] = fmaxf(mx[ni], x);
+      }
   }
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
@@ -139,25 +177,27 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const Fw
     if (lane < 32) red[wm * 256 + wn * 128 + ni * 32 + lane] = mx[ni];
   }
   __syncthreads();
+  // Pass 2: s = sum 2^d2, q = sum 2^d2 * d2 with d2 = (z - M) log2(e) = x c1 log2(e) - M log2(e).
+  const float c1l = a.c1 * kLog2e;
+  float ml[4];
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
     const int tn = wn * 128 + ni * 32 + (lane & 31);
-    mx[ni] = fmaxf(red[tn], red[256 + tn]);
+    mx[ni] = fmaxf(red[tn], red[256 + tn]) * a.c1;
+    ml[ni] = mx[ni] * kLog2e;
   }
-  // Pass 2: s = sum 2^d2, q = sum 2^d2 * d2 with d2 = (z - M) log2(e), in register order.
   float sv[4] = {0.f, 0.f, 0.f, 0.f}, qv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     float b[16];
-    load_bias16<TAIL>(a.bias, a.bias_f32, vbase + mi * 32, lane, a.n_real, b);
+    bias16<BMODE, TAIL>(a.bias, vbase + mi * 32, lane, a.n_real, b);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float z = zval<TAIL>(acc[mi][ni][r], b, r, hb, a.c1,
-                                   vbase + mi * 32 + mfma_row(r, lane), a.n_real);
-        float d2 = (z - mx[ni]) * kLog2e;
-        if (TAIL) d2 = fmaxf(d2, -1e30f);  // excluded column: exp2 -> 0 and 0 * d2 -> 0
+        float d2 = fmaf(xval<BMODE>(acc[mi][ni][r], b, r), c1l, -ml[ni]);
+        // Excluded column: 2^-1e30 = 0 and 0 * -1e30 = 0.
+        if (TAIL && vbase + mi * 32 + mfma_row(r, lane) >= a.n_real) d2 = -1e30f;
         const float e = __builtin_amdgcn_exp2f(d2);
         sv[ni] += e;
         qv[ni] = fmaf(e, d2, qv[ni]);
@@ -198,13 +238,8 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const Fw
         for (int r = 0; r < 16; ++r)
           if (mi == mt && r == rt) t = acc[mi][ni][r];
       if (mine) {
-        float bt = 0.f;
-        if (hb) {
-          const int v = vbase + tl;
-          bt = a.bias_f32 ? reinterpret_cast<const float*>(a.bias)[v]
-                          : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[v]);
-        }
-        a.tz[j] = hb ? (t + bt) * a.c1 : t * a.c1;
+        if constexpr (BMODE != BIAS_NONE) t += bias1<BMODE>(a.bias, vbase + tl);
+        a.tz[j] = t * a.c1;
       }
     }
   }
@@ -235,10 +270,17 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   f32x16 acc[4][4];
   zero_acc(acc);
   dma::mainloop(la, lb, 0, a.H / dma::BKD, smem, acc);
-  if (v0 + BM > a.n_real)
-    fwd_epilogue<true>(acc, a, vt, v0, j0, Ts, smem);
-  else
-    fwd_epilogue<false>(acc, a, vt, v0, j0, Ts, smem);
+  const bool tail = v0 + BM > a.n_real;
+  if (a.bias == nullptr) {
+    if (tail) fwd_epilogue<true, BIAS_NONE>(acc, a, vt, v0, j0, Ts, smem);
+    else fwd_epilogue<false, BIAS_NONE>(acc, a, vt, v0, j0, Ts, smem);
+  } else if (a.bias_f32) {
+    if (tail) fwd_epilogue<true, BIAS_F32>(acc, a, vt, v0, j0, Ts, smem);
+    else fwd_epilogue<false, BIAS_F32>(acc, a, vt, v0, j0, Ts, smem);
+  } else {
+    if (tail) fwd_epilogue<true, BIAS_BF16>(acc, a, vt, v0, j0, Ts, smem);
+    else fwd_epilogue<false, BIAS_BF16>(acc, a, vt, v0, j0, Ts, smem);
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -467,68 +509,10 @@ constexpr int GT_STRIDE = BN + 8;  // padded LDS row (bf16 elements) of the stag
 constexpr int GRAD_LDS_BYTES = BN * GT_STRIDE * 2;
 constexpr int BWDG_LDS_BYTES = GRAD_LDS_BYTES > dma::LDS_BYTES ? GRAD_LDS_BYTES : dma::LDS_BYTES;
 
-template <bool TAIL>
-__device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArgs& a, int v0,
-                                              int j0, int Ts, uint16_t* smem) {
+// Writes the staged bf16 tile Gs[token][vocab] (LDS) as G rows and Gt rows.
+__device__ __forceinline__ void grad_store(const GradArgs& a, int v0, int j0, int Ts,
+                                           const uint16_t* smem) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int vbase = v0 + wm * 128;
-  float lse[4], dl[4], de[4], ez[4];
-  int tl[4];
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int j = j0 + wn * 128 + ni * 32 + (lane & 31);
-    const int jj = j < Ts ? j : Ts - 1;
-    const int row = a.scored[jj];
-    lse[ni] = a.lse[row];
-    dl[ni] = a.dlogp[row];
-    de[ni] = a.dent ? a.dent[row] : 0.f;
-    ez[ni] = a.dent ? lse[ni] - a.ent[row] : 0.f;
-    tl[ni] = a.tloc[jj] - vbase;
-    if (j >= Ts) dl[ni] = de[ni] = 0.f;  // rows past the count: exact zeros in G and Gt
-  }
-  // Stage the bf16 tile as Gs[token][vocab] in LDS, then write full rows.
-  __syncthreads();
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    float b[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int v = vbase + mi * 32 + mfma_row(r, lane);
-      b[r] = 0.f;
-      if (a.bias != nullptr && v < a.n_real)
-        b[r] = a.bias_f32 ? reinterpret_cast<const float*>(a.bias)[v]
-                          : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[v]);
-    }
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int tn = wn * 128 + ni * 32 + (lane & 31);
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        uint32_t pk[2];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = rg * 4 + u;
-          const int vl = mi * 32 + mfma_row(r, lane);
-          const float av = acc_read(acc[mi][ni][r]);
-          const float z = a.bias != nullptr ? (av + b[r]) * a.c1 : av * a.c1;
-          const float p = __builtin_amdgcn_exp2f((z - lse[ni]) * kLog2e);
-          float g = dl[ni] * ((vl == tl[ni] ? 1.f : 0.f) - p);
-          if (a.dent) g -= de[ni] * p * (z - ez[ni]);
-          if (dl[ni] == 0.f && de[ni] == 0.f) g = 0.f;  // no gradient flows: exact 0
-          g *= a.c1;
-          if (TAIL && vbase + vl >= a.n_real) g = 0.f;
-          const uint32_t hb = f32_to_bf16_rne(g);
-          if (u & 1)
-            pk[u >> 1] |= hb << 16;
-          else
-            pk[u >> 1] = hb;
-        }
-        const int vl0 = wm * 128 + mi * 32 + mfma_row(rg * 4, lane);
-        *reinterpret_cast<uint2*>(smem + tn * GT_STRIDE + vl0) = make_uint2(pk[0], pk[1]);
-      }
-    }
-  }
   __syncthreads();
   // G[j][v0 .. v0+255] for the scored rows of the tile (K = vocabulary for dhidden).
   for (int idx = threadIdx.x; idx < BN * (BM / 8); idx += NTHREADS) {
@@ -557,6 +541,67 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArg
   }
 }
 
+template <bool TAIL, int BMODE, bool ENT>
+__device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArgs& a, int v0,
+                                              int j0, int Ts, uint16_t* smem) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int vbase = v0 + wm * 128;
+  const float c1l = a.c1 * kLog2e;
+  float lsel[4], dl[4], de[4], ez[4];
+  int tl[4];
+  bool live[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int j = j0 + wn * 128 + ni * 32 + (lane & 31);
+    const int jj = j < Ts ? j : Ts - 1;
+    const int row = a.scored[jj];
+    const float lse = a.lse[row];
+    lsel[ni] = lse * kLog2e;
+    dl[ni] = a.dlogp[row];
+    de[ni] = ENT ? a.dent[row] : 0.f;
+    ez[ni] = ENT ? lse - a.ent[row] : 0.f;
+    tl[ni] = a.tloc[jj] - vbase;
+    // Rows past the count, and rows no gradient flows into, are exact zeros in G and Gt.
+    live[ni] = j < Ts && (dl[ni] != 0.f || de[ni] != 0.f);
+  }
+  // Stage the bf16 tile as Gs[token][vocab] in LDS, then write full rows.
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    float b[16];
+    bias16<BMODE, TAIL>(a.bias, vbase + mi * 32, lane, a.n_real, b);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int tn = wn * 128 + ni * 32 + (lane & 31);
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        uint32_t pk[2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = rg * 4 + u;
+          const int vl = mi * 32 + mfma_row(r, lane);
+          const float x = xval<BMODE>(acc_read(acc[mi][ni][r]), b, r);
+          // p = exp(z - lse) = 2^(x c1 log2(e) - lse log2(e)).
+          const float p = __builtin_amdgcn_exp2f(fmaf(x, c1l, -lsel[ni]));
+          float g = dl[ni] * ((vl == tl[ni] ? 1.f : 0.f) - p);
+          if constexpr (ENT) g -= de[ni] * p * (x * a.c1 - ez[ni]);
+          g *= a.c1;
+          if (!live[ni] || (TAIL && vbase + vl >= a.n_real)) g = 0.f;
+          const uint32_t hb = f32_to_bf16_rne(g);
+          if (u & 1)
+            pk[u >> 1] |= hb << 16;
+          else
+            pk[u >> 1] = hb;
+        }
+        const int vl0 = wm * 128 + mi * 32 + mfma_row(rg * 4, lane);
+        *reinterpret_cast<uint2*>(smem + tn * GT_STRIDE + vl0) = make_uint2(pk[0], pk[1]);
+      }
+    }
+  }
+  grad_store(a, v0, j0, Ts, smem);
+}
+
 __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_grad(GradArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[BWDG_LDS_BYTES / 2];
   int vt, tb;
@@ -578,10 +623,20 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   f32x16 acc[4][4];
   zero_acc(acc);
   dma::mainloop(la, lb, 0, a.H / dma::BKD, smem, acc);
-  if (v0 + BM > a.n_real)
-    grad_epilogue<true>(acc, a, v0, j0, Ts, smem);
-  else
-    grad_epilogue<false>(acc, a, v0, j0, Ts, smem);
+  const bool tail = v0 + BM > a.n_real, ent = a.dent != nullptr;
+  const int bmode = a.bias == nullptr ? BIAS_NONE : a.bias_f32 ? BIAS_F32 : BIAS_BF16;
+#define LLP_GRAD_EPI(BM_, ENT_)                                          \
+  if (bmode == BM_ && ent == ENT_) {                                      \
+    if (tail) grad_epilogue<true, BM_, ENT_>(acc, a, v0, j0, Ts, smem);   \
+    else grad_epilogue<false, BM_, ENT_>(acc, a, v0, j0, Ts, smem);       \
+  }
+  LLP_GRAD_EPI(BIAS_NONE, false)
+  LLP_GRAD_EPI(BIAS_NONE, true)
+  LLP_GRAD_EPI(BIAS_BF16, false)
+  LLP_GRAD_EPI(BIAS_BF16, true)
+  LLP_GRAD_EPI(BIAS_F32, false)
+  LLP_GRAD_EPI(BIAS_F32, true)
+#undef LLP_GRAD_EPI
 }
 
 // dhidden partials: P[split][j][n] = sum over the split's K range of G[j, k] WT[n, k]

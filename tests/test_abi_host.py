@@ -147,6 +147,12 @@ BAD_FORWARD = [
     ("bad bias dtype", lambda r: (setattr(r.proj, "bias", FAKE), setattr(r.proj, "bias_dtype", 7)),
      A.LLP_ERR_INVALID_ARGUMENT),
     ("unknown flag", lambda r: setattr(r, "flags", 2), A.LLP_ERR_INVALID_ARGUMENT),
+    ("f32 bias misaligned", lambda r: (setattr(r.proj, "bias", FAKE + 8),
+                                       setattr(r.proj, "bias_dtype", A.LLP_DTYPE_F32)),
+     A.LLP_ERR_INVALID_ARGUMENT),
+    ("bf16 bias misaligned", lambda r: (setattr(r.proj, "bias", FAKE + 4),
+                                        setattr(r.proj, "bias_dtype", A.LLP_DTYPE_BF16)),
+     A.LLP_ERR_INVALID_ARGUMENT),
 ]
 
 
