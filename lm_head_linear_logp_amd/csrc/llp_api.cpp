@@ -71,7 +71,7 @@ llp_status check_request(const llp_request* req) {
   const llp_projection& p = req->proj;
   const int64_t T = req->layout.num_tokens;
   LLP_CHECK(T >= 0, LLP_ERR_INVALID_ARGUMENT, "num_tokens=%lld < 0", (long long)T);
-  LLP_CHECK(T < (int64_t(1) << 31) - 256, LLP_ERR_UNSUPPORTED, "num_tokens %lld too large",
+  LLP_CHECK(T <= (int64_t(1) << 23) - 256, LLP_ERR_UNSUPPORTED, "num_tokens %lld too large",
             (long long)T);
   llp_status st = check_partition(req->vocab);
   if (st != LLP_OK) return st;
@@ -84,6 +84,13 @@ llp_status check_request(const llp_request* req) {
   LLP_CHECK(p.weight_stride >= p.hidden_size && p.weight_stride % 8 == 0,
             LLP_ERR_INVALID_ARGUMENT, "weight_stride %lld must be >= H and a multiple of 8",
             (long long)p.weight_stride);
+  // Operand rows are addressed with 32-bit byte offsets from a tile's first row.
+  LLP_CHECK(p.hidden_stride < (int64_t(1) << 23) && p.weight_stride < (int64_t(1) << 23),
+            LLP_ERR_UNSUPPORTED, "hidden_stride and weight_stride must be < 2^23");
+  LLP_CHECK(T * p.hidden_stride <= (int64_t(1) << 31), LLP_ERR_UNSUPPORTED,
+            "T * hidden_stride = %lld exceeds 2^31", (long long)(T * p.hidden_stride));
+  LLP_CHECK(req->vocab.local_size <= (int64_t(1) << 23) - 256, LLP_ERR_UNSUPPORTED,
+            "local_size %lld exceeds 2^23 - 256", (long long)req->vocab.local_size);
   if (T > 0) {
     LLP_CHECK(p.hidden != nullptr, LLP_ERR_INVALID_ARGUMENT, "proj.hidden is NULL");
     LLP_CHECK(aligned(p.hidden, 16), LLP_ERR_INVALID_ARGUMENT, "proj.hidden not 16-byte aligned");

@@ -245,6 +245,27 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const Fw
   }
 }
 
+// Loaders of the fused tiles: weight rows v0 .. (clamped below n_real) and the scored hidden
+// rows j0 .. (clamped below the count), gathered through `scored` (ascending). The hidden
+// resource starts at the tile's first scored row; the host keeps T * hidden_stride * 2 below
+// 2^31 bytes, so every lane offset fits in 32 bits.
+__device__ __forceinline__ void weight_hidden_loaders(const uint16_t* W, int64_t ldw, int64_t n_real,
+                                                      int v0, const uint16_t* h, int64_t ldh,
+                                                      const int32_t* scored, int j0, int Ts, int H,
+                                                      dma::Loader& la, dma::Loader& lb) {
+  const int nv = n_real - v0 < BM ? (int)(n_real - v0) : BM;
+  const int nj = Ts - j0 < BN ? Ts - j0 : BN;
+  const int64_t h0 = scored[j0];
+  la.init(W + (int64_t)v0 * ldw, (uint64_t)((nv - 1) * ldw + H) * 2);
+  lb.init(h + h0 * ldh, (uint64_t)((scored[j0 + nj - 1] - h0) * ldh + H) * 2);
+#pragma unroll
+  for (int u = 0; u < dma::NI; ++u) {
+    const int r = dma::Loader::row_of(u);
+    la.set(u, r < nv ? r : nv - 1, ldw);
+    lb.set(u, scored[j0 + (r < nj ? r : nj - 1)] - h0, ldh);
+  }
+}
+
 // The epilogue reuses the pipeline's LDS for 6 x 256 fp32 partials.
 static_assert(6 * 256 * 4 <= dma::LDS_BYTES, "forward epilogue LDS");
 static_assert(dma::BKD == KSTEP, "K step shared with the host");
@@ -257,16 +278,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int j0 = tb * BN, v0 = vt * BM;
   if (j0 >= Ts) return;
   dma::Loader la, lb;
-#pragma unroll
-  for (int u = 0; u < dma::NI; ++u) {
-    const int r = dma::Loader::row_of(u), c = dma::Loader::chunk_of(u);
-    int v = v0 + r;
-    v = v < a.n_real ? v : (int)a.n_real - 1;
-    la.p[u] = a.W + (int64_t)v * a.ldw + c * 8;
-    int j = j0 + r;
-    j = j < Ts ? j : Ts - 1;
-    lb.p[u] = a.h + (int64_t)a.scored[j] * a.ldh + c * 8;
-  }
+  weight_hidden_loaders(a.W, a.ldw, a.n_real, v0, a.h, a.ldh, a.scored, j0, Ts, a.H, la, lb);
   f32x16 acc[4][4];
   zero_acc(acc);
   dma::mainloop(la, lb, 0, a.H / dma::BKD, smem, acc);
@@ -610,16 +622,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int j0 = tb * BN, v0 = vt * BM;
   if (j0 >= Ts) return;
   dma::Loader la, lb;
-#pragma unroll
-  for (int u = 0; u < dma::NI; ++u) {
-    const int r = dma::Loader::row_of(u), c = dma::Loader::chunk_of(u);
-    int v = v0 + r;
-    v = v < a.n_real ? v : (int)a.n_real - 1;
-    la.p[u] = a.W + (int64_t)v * a.ldw + c * 8;
-    int j = j0 + r;
-    j = j < Ts ? j : Ts - 1;
-    lb.p[u] = a.h + (int64_t)a.scored[j] * a.ldh + c * 8;
-  }
+  weight_hidden_loaders(a.W, a.ldw, a.n_real, v0, a.h, a.ldh, a.scored, j0, Ts, a.H, la, lb);
   f32x16 acc[4][4];
   zero_acc(acc);
   dma::mainloop(la, lb, 0, a.H / dma::BKD, smem, acc);
@@ -652,13 +655,17 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int Ts = *a.count;
   const int j0 = mt * BM, n0 = nt * BN;
   if (j0 >= Ts) return;
+  // G rows j0 .. j0+255 (all inside the workspace's row capacity) and WT rows n0 .. (< H).
+  const int nn = a.H - n0 < BN ? a.H - n0 : BN;
+  const int64_t kb = (int64_t)a.nks * dma::BKD;
   dma::Loader la, lb;
+  la.init(a.G + (int64_t)j0 * a.ldg, (uint64_t)((BM - 1) * a.ldg + kb) * 2);
+  lb.init(a.WT + (int64_t)n0 * a.ldwt, (uint64_t)((nn - 1) * a.ldwt + kb) * 2);
 #pragma unroll
   for (int u = 0; u < dma::NI; ++u) {
-    const int r = dma::Loader::row_of(u), c = dma::Loader::chunk_of(u);
-    la.p[u] = a.G + (int64_t)(j0 + r) * a.ldg + c * 8;
-    const int n = n0 + r < a.H ? n0 + r : a.H - 1;
-    lb.p[u] = a.WT + (int64_t)n * a.ldwt + c * 8;
+    const int r = dma::Loader::row_of(u);
+    la.set(u, r, a.ldg);
+    lb.set(u, r < nn ? r : nn - 1, a.ldwt);
   }
   const int ks0 = (int)((int64_t)a.nks * sp / a.nsplit);
   const int ks1 = (int)((int64_t)a.nks * (sp + 1) / a.nsplit);
@@ -714,13 +721,18 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int Ts = *a.count;
   if (Ts <= 0) return;
   const int m0 = mt * BM, n0 = nt * BN;
+  // Gt rows m0 .. m0+255 (inside the padded vocabulary capacity) and hgT rows n0 .. (< H);
+  // K = scored rows rounded up to whole steps (both are zero there, up to the token tile).
+  const int nn = a.H - n0 < BN ? a.H - n0 : BN;
+  const int64_t kb = (int64_t)((Ts + dma::BKD - 1) / dma::BKD) * dma::BKD;
   dma::Loader la, lb;
+  la.init(a.Gt + (int64_t)m0 * a.ldk, (uint64_t)((BM - 1) * a.ldk + kb) * 2);
+  lb.init(a.hgT + (int64_t)n0 * a.ldk, (uint64_t)((nn - 1) * a.ldk + kb) * 2);
 #pragma unroll
   for (int u = 0; u < dma::NI; ++u) {
-    const int r = dma::Loader::row_of(u), c = dma::Loader::chunk_of(u);
-    la.p[u] = a.Gt + (int64_t)(m0 + r) * a.ldk + c * 8;
-    const int n = n0 + r < a.H ? n0 + r : a.H - 1;
-    lb.p[u] = a.hgT + (int64_t)n * a.ldk + c * 8;
+    const int r = dma::Loader::row_of(u);
+    la.set(u, r, a.ldk);
+    lb.set(u, r < nn ? r : nn - 1, a.ldk);
   }
   f32x16 acc[4][4];
   zero_acc(acc);

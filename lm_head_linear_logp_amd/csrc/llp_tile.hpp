@@ -104,8 +104,13 @@ constexpr int LDS_BYTES = NST * 2 * STAGE * 2;
 
 __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
 
+// One operand's loads: a buffer resource whose base is the operand's first row in the tile, and
+// per load instruction this lane's 32-bit byte offset at K step 0; the K step's offset goes in
+// the instruction's scalar offset. Offsets are exact (rows clamped by the caller), so every
+// access lies inside [base, base + bytes), the range given to the resource.
 struct Loader {
-  const uint16_t* p[NI];  // per instruction: this lane's global address at K step 0
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff[NI];
 
   __device__ __forceinline__ static int row_of(int u) {
     return 64 * (threadIdx.x >> 6) + 8 * u + ((threadIdx.x & 63) >> 3);
@@ -113,13 +118,23 @@ struct Loader {
   __device__ __forceinline__ static int chunk_of(int u) {
     return (threadIdx.x & 7) ^ swz8(row_of(u));
   }
+  // Raw buffer (stride 0) over `bytes` bytes from `base` (gfx9 resource word 3: 32-bit data).
+  __device__ __forceinline__ void init(const uint16_t* base, uint64_t bytes) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
+                                             (int)(uint32_t)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull),
+                                             0x00020000);
+  }
+  // Instruction u reads row `row` (relative to the base, row stride `ld` elements) for this lane.
+  __device__ __forceinline__ void set(int u, int64_t row, int64_t ld) {
+    voff[u] = (uint32_t)((row * ld + chunk_of(u) * 8) * 2);
+  }
   // One DMA instruction (u = 0..NI-1) of this wave for K step `kstep` into `stage`.
   __device__ __forceinline__ void issue1(uint16_t* stage, int kstep, int u) const {
     // The wave index is uniform: keep the LDS destination (M0) in scalar registers.
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    __builtin_amdgcn_global_load_lds(
-        (const void*)(p[u] + kstep * BKD),
-        (__attribute__((address_space(3))) void*)(stage + (64 * w + 8 * u) * BKD), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(stage + (64 * w + 8 * u) * BKD), 16,
+        voff[u], kstep * (BKD * 2), 0, 0);
   }
   __device__ __forceinline__ void issue(uint16_t* stage, int kstep) const {
 #pragma unroll

@@ -147,6 +147,12 @@ BAD_FORWARD = [
     ("bad bias dtype", lambda r: (setattr(r.proj, "bias", FAKE), setattr(r.proj, "bias_dtype", 7)),
      A.LLP_ERR_INVALID_ARGUMENT),
     ("unknown flag", lambda r: setattr(r, "flags", 2), A.LLP_ERR_INVALID_ARGUMENT),
+    ("T too large", lambda r: setattr(r.layout, "num_tokens", 1 << 23), A.LLP_ERR_UNSUPPORTED),
+    ("hidden bytes > 4 GiB", lambda r: (setattr(r.layout, "num_tokens", 1 << 20),
+                                        setattr(r.proj, "hidden_stride", 4096)), A.LLP_ERR_UNSUPPORTED),
+    ("weight stride >= 2^23", lambda r: setattr(r.proj, "weight_stride", 1 << 23), A.LLP_ERR_UNSUPPORTED),
+    ("shard too large", lambda r: (setattr(r.vocab, "padded_vocab", 1 << 24), setattr(r.vocab, "local_size", 1 << 24),
+                                   setattr(r.vocab, "real_vocab", 1 << 24)), A.LLP_ERR_UNSUPPORTED),
     ("f32 bias misaligned", lambda r: (setattr(r.proj, "bias", FAKE + 8),
                                        setattr(r.proj, "bias_dtype", A.LLP_DTYPE_F32)),
      A.LLP_ERR_INVALID_ARGUMENT),
