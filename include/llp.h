@@ -205,7 +205,8 @@ typedef struct {
  *   dhidden  bf16 [T, H], row stride dhidden_stride (>= H, multiple of 8): OVERWRITTEN with
  *            this shard's contribution G . weight (unscored rows 0). With world > 1 the caller
  *            sums the shards' dhidden.
- *   dweight  fp32 [local_size, H], row stride dweight_stride (>= H): ACCUMULATED (+=) with
+ *   dweight  fp32 [local_size, H], row stride dweight_stride (>= H, multiple of 4, < 2^21,
+ *            else INVALID_ARGUMENT / UNSUPPORTED), 16-byte aligned base: ACCUMULATED (+=) with
  *            G^T . hidden over this call's rows; padding rows untouched.
  *   dbias    fp32 [local_size] ACCUMULATED, or NULL.
  * G[t, v] = (dlogp_t (1[v = target_t] - p_tv) - dentropy_t p_tv (z_tv - E_p z_t)) / temperature

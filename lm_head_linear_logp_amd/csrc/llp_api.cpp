@@ -383,6 +383,10 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
   if (req->vocab.local_size > 0) {
     LLP_CHECK(out->dweight != nullptr, LLP_ERR_INVALID_ARGUMENT, "out.dweight is NULL");
     LLP_CHECK(out->dweight_stride >= H, LLP_ERR_INVALID_ARGUMENT, "dweight_stride must be >= H");
+    LLP_CHECK(out->dweight_stride % 4 == 0 && aligned(out->dweight, 16), LLP_ERR_INVALID_ARGUMENT,
+              "dweight needs a 16-byte aligned base and a stride that is a multiple of 4");
+    LLP_CHECK(out->dweight_stride < (int64_t(1) << 21), LLP_ERR_UNSUPPORTED,
+              "dweight_stride must be < 2^21");
   }
   const Ws w = ws_layout(T, n_real, H, LLP_OP_BACKWARD);
   LLP_CHECK(workspace_bytes >= w.total, LLP_ERR_INVALID_ARGUMENT,

@@ -712,6 +712,82 @@ __global__ __launch_bounds__(256) void k_dh_reduce(DhReduceArgs a) {
   *reinterpret_cast<u32x4*>(a.dH + t * a.ldd + n) = u32x4{pk[0], pk[1], pk[2], pk[3]};
 }
 
+// dweight[m0 .. m0+255, n0 .. n0+255] += acc, through LDS (the pipeline's stages are free
+// here). Four phases, one per 32-row block mi of every wave: phase p covers tile rows
+// wm*128 + 32p + (0..31) for wm = 0, 1, i.e. 64 rows of 1 KiB. Its old values arrive by direct
+// global->LDS loads (no registers, a whole phase in flight; phases p+1, p+2 stream in while p
+// is summed, two 64 KiB buffers); each lane adds its accumulators in place, then every wave
+// writes 16 whole rows back with 16-byte stores. Rows at or past n_real and columns at or past
+// H are neither read into a result nor written (their loads read a clamped in-bounds address).
+constexpr int DWB_ROWS = 64;                 // rows per phase
+constexpr int DWB_BYTES = DWB_ROWS * BN * 4;  // 64 KiB per phase buffer
+static_assert(2 * DWB_BYTES <= dma::LDS_BYTES, "dweight staging fits the pipeline LDS");
+
+__device__ __forceinline__ void dw_phase_load(const DwArgs& a, int m0, int n0, int nv, int nc, int p,
+                                              unsigned char* buf) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.dW + (int64_t)m0 * a.lddw + n0), (short)0,
+      (int)(uint32_t)(((int64_t)(nv - 1) * a.lddw + nc) * 4), 0x00020000);
+  const uint32_t voff = 4 * lane < nc ? 16u * lane : 0u;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int q = 16 * w + u;                          // phase row (uniform)
+    int lr = (q >> 5) * 128 + 32 * p + (q & 31);       // tile row
+    lr = lr < nv ? lr : nv - 1;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(buf + q * (BN * 4)), 16, voff,
+        (int)((int64_t)lr * a.lddw * 4), 0, 0);
+  }
+}
+
+__device__ __forceinline__ void dw_accumulate(const f32x16 (&acc)[4][4], const DwArgs& a, int m0,
+                                              int n0, uint16_t* smem) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  const int nv = a.n_real - m0 < BM ? (int)(a.n_real - m0) : BM;
+  const int nc = a.H - n0 < BN ? a.H - n0 : BN;
+  unsigned char* lds = reinterpret_cast<unsigned char*>(smem);
+  // VMEM order per wave: L0 L1 | S0 L2 | S1 L3 | S2 | S3, 16 loads per L and at most 16 stores
+  // per S (a wave skips the stores of rows past n_real). Completion is in order, so phase p's
+  // loads (and the stores before them) have landed once at most 16 instructions are pending
+  // for p < 3 (exactly the 16 loads of phase p+1 or p+2 were issued after them) and 0 for p = 3.
+  dw_phase_load(a, m0, n0, nv, nc, 0, lds);
+  dw_phase_load(a, m0, n0, nv, nc, 1, lds + DWB_BYTES);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    unsigned char* buf = lds + (p & 1) * DWB_BYTES;
+    if (p < 3) dma::wait_vmem_le<16>();
+    else dma::wait_vmem_le<0>();
+    dma::lds_barrier();
+    // In place: buf[row][col] += acc for this lane's 64 elements of block mi = p.
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = wm * 32 + mfma_row(r, lane);
+        const int c = wn * 128 + ni * 32 + (lane & 31);
+        float* e = reinterpret_cast<float*>(buf + q * (BN * 4) + c * 4);
+        *e += acc_read(acc[p][ni][r]);
+      }
+    dma::lds_barrier();
+    // Wave w writes phase rows 16w .. 16w+15, 16 bytes per lane.
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int q = 16 * wave + u;
+      const int lr = (q >> 5) * 128 + 32 * p + (q & 31);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(buf + q * (BN * 4) + 16 * lane);
+      if (lr < nv && 4 * lane < nc)
+        *reinterpret_cast<u32x4*>(a.dW + (int64_t)(m0 + lr) * a.lddw + n0 + 4 * lane) = v;
+    }
+    if (p + 2 < 4) {
+      dma::lds_barrier();  // every wave has read this buffer
+      dw_phase_load(a, m0, n0, nv, nc, p + 2, buf);
+    }
+  }
+  dma::wait_vmem_le<0>();
+}
+
 // dweight[v, n] += sum_j Gt[v, j] hgT[n, j] over the scored rows j in ascending order
 // (Gt and hgT are zero past the count up to the token tile, so whole K steps can be used).
 __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dw(DwArgs a) {
@@ -737,44 +813,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   f32x16 acc[4][4];
   zero_acc(acc);
   dma::mainloop(la, lb, 0, (Ts + dma::BKD - 1) / dma::BKD, smem, acc);
-  // dweight += acc, 64 values per row block mi; the loads of block mi+1 are issued before the
-  // adds and stores of block mi so that HBM latency is paid about once per tile.
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
-  const bool full = m0 + BM <= a.n_real && n0 + BN <= a.H;
-  float cur[4][16], nxt[4][16];
-  auto ptr = [&](int mi, int ni, int r) {
-    const int v = m0 + wm * 128 + mi * 32 + mfma_row(r, lane);
-    const int n = n0 + wn * 128 + ni * 32 + (lane & 31);
-    return a.dW + (int64_t)v * a.lddw + n;
-  };
-  auto ok = [&](int mi, int ni, int r) {
-    const int v = m0 + wm * 128 + mi * 32 + mfma_row(r, lane);
-    const int n = n0 + wn * 128 + ni * 32 + (lane & 31);
-    return full || (v < a.n_real && n < a.H);
-  };
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) cur[ni][r] = ok(0, ni, r) ? *ptr(0, ni, r) : 0.f;
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    if (mi + 1 < 4) {
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) nxt[ni][r] = ok(mi + 1, ni, r) ? *ptr(mi + 1, ni, r) : 0.f;
-    }
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (ok(mi, ni, r)) *ptr(mi, ni, r) = cur[ni][r] + acc_read(acc[mi][ni][r]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) cur[ni][r] = nxt[ni][r];
-  }
+  dw_accumulate(acc, a, m0, n0, smem);
 }
 
 // out[c][r] = in[row(r)][c] for r < nvalid (zero for nvalid <= r < the grid's rows), 64 x 64

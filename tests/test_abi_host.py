@@ -277,3 +277,14 @@ def test_backward_validation():
     bo.dweight = FAKE
     bi.lse = None
     assert call() == A.LLP_ERR_INVALID_ARGUMENT
+
+
+def test_backward_rejects_bad_dweight_layout():
+    lib = A.load()
+    r = good_request()
+    bi = A.llp_bwd_in(FAKE, FAKE, None, None)
+    call = lambda bo: lib.llp_backward(C.byref(r), C.byref(bi), C.byref(bo), FAKE, 1 << 40, None)
+    # stride not a multiple of 4, misaligned base, stride beyond the 32-bit offset envelope
+    assert call(A.llp_bwd_out(FAKE, 4096, FAKE, 4098, None)) == A.LLP_ERR_INVALID_ARGUMENT
+    assert call(A.llp_bwd_out(FAKE, 4096, FAKE + 4, 4096, None)) == A.LLP_ERR_INVALID_ARGUMENT
+    assert call(A.llp_bwd_out(FAKE, 4096, FAKE, 1 << 21, None)) == A.LLP_ERR_UNSUPPORTED
