@@ -270,6 +270,9 @@ __device__ __forceinline__ void weight_hidden_loaders(const uint16_t* W, int64_t
 static_assert(6 * 256 * 4 <= dma::LDS_BYTES, "forward epilogue LDS");
 static_assert(dma::BKD == KSTEP, "K step shared with the host");
 
+// One kernel per bias mode: each gets its own register allocation (the bias variants need
+// more registers in the epilogue than the common no-bias case).
+template <int BMODE>
 __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
   int vt, tb;
@@ -282,17 +285,10 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   f32x16 acc[4][4];
   zero_acc(acc);
   dma::mainloop(la, lb, 0, a.H / dma::BKD, smem, acc);
-  const bool tail = v0 + BM > a.n_real;
-  if (a.bias == nullptr) {
-    if (tail) fwd_epilogue<true, BIAS_NONE>(acc, a, vt, v0, j0, Ts, smem);
-    else fwd_epilogue<false, BIAS_NONE>(acc, a, vt, v0, j0, Ts, smem);
-  } else if (a.bias_f32) {
-    if (tail) fwd_epilogue<true, BIAS_F32>(acc, a, vt, v0, j0, Ts, smem);
-    else fwd_epilogue<false, BIAS_F32>(acc, a, vt, v0, j0, Ts, smem);
-  } else {
-    if (tail) fwd_epilogue<true, BIAS_BF16>(acc, a, vt, v0, j0, Ts, smem);
-    else fwd_epilogue<false, BIAS_BF16>(acc, a, vt, v0, j0, Ts, smem);
-  }
+  if (v0 + BM > a.n_real)
+    fwd_epilogue<true, BMODE>(acc, a, vt, v0, j0, Ts, smem);
+  else
+    fwd_epilogue<false, BMODE>(acc, a, vt, v0, j0, Ts, smem);
 }
 
 // ------------------------------------------------------------------------------------
@@ -872,7 +868,12 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
-  if (a.nvt > 0 && a.ntb > 0) hipLaunchKernelGGL(k_fwd, dim3(a.nvt * a.ntb), dim3(NTHREADS), 0, s, a);
+  if (a.nvt > 0 && a.ntb > 0) {
+    const dim3 grid(a.nvt * a.ntb), block(NTHREADS);
+    if (a.bias == nullptr) hipLaunchKernelGGL(k_fwd<BIAS_NONE>, grid, block, 0, s, a);
+    else if (a.bias_f32) hipLaunchKernelGGL(k_fwd<BIAS_F32>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(k_fwd<BIAS_BF16>, grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -928,7 +929,7 @@ hipError_t launch_dbias(const DbArgs& a, hipStream_t s) {
 
 hipError_t probe_kernels() {
   hipFuncAttributes attr;
-  return hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(k_fwd));
+  return hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(k_fwd<BIAS_NONE>));
 }
 
 }  // namespace llp
