@@ -513,8 +513,12 @@ __global__ __launch_bounds__(256) void k_topp(ToppArgs a) {
 // dhidden = G W (split over K = vocabulary in a fixed number of fixed ranges, partials
 // summed in range order) and dweight += G^T h over the scored rows in order, db += sum_j G.
 // ------------------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 constexpr int GT_STRIDE = BN + 8;  // padded LDS row (bf16 elements) of the staged G tile
-constexpr int GRAD_LDS_BYTES = BN * GT_STRIDE * 2;
+constexpr int GS_BYTES = BN * GT_STRIDE * 2;
+constexpr int GT_STAGE_BYTES = 32 * 128;  // per wave: 32 rows x 64 tokens of Gt
+constexpr int GRAD_LDS_BYTES = GS_BYTES + 4 * GT_STAGE_BYTES;
+static_assert(GRAD_LDS_BYTES <= 160 * 1024, "gradient tile LDS");
 constexpr int BWDG_LDS_BYTES = GRAD_LDS_BYTES > dma::LDS_BYTES ? GRAD_LDS_BYTES : dma::LDS_BYTES;
 
 // Writes the staged bf16 tile Gs[token][vocab] (LDS) as G rows and Gt rows.
@@ -530,22 +534,47 @@ __device__ __forceinline__ void grad_store(const GradArgs& a, int v0, int j0, in
       *reinterpret_cast<u32x4*>(a.G + (int64_t)j * a.ldg + v0 + c * 8) =
           *reinterpret_cast<const u32x4*>(smem + tn * GT_STRIDE + c * 8);
   }
-  // Gt[v][j0 .. j0+255] (K = scored row for dweight), zeros past the count: wave w writes
-  // the 64 columns 64w .. 64w+63 of vocabulary rows lane + 64c, one 128-byte line per lane.
+  // Gt[v][j0 .. j0+255] (K = scored row for dweight), zeros past the count. Wave w owns tokens
+  // 64w .. 64w+63 and does 64 vocabulary rows per pass c. ds_read_b64_tr_b16 transposes within
+  // each 16-lane group: source lane 4j + t reads 4 vocabulary values (quad t) of token row j,
+  // and output lane i receives the 4 tokens' values of vocabulary column i (element i % 4 of
+  // source lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4). Lane (g, i) so collects the wave's 64 tokens
+  // of row 64c + 16g + i (128 bytes); half a pass at a time, those rows go through a per-wave
+  // LDS area (16-byte pieces XOR-swizzled by row) so that each store writes 8 whole lines.
+  const int g = lane >> 4, i = lane & 15, sj = i >> 2, st = i & 3;
+  unsigned char* stg = reinterpret_cast<unsigned char*>(const_cast<uint16_t*>(smem)) + GS_BYTES +
+                       wave * GT_STAGE_BYTES;
 #pragma unroll 1
   for (int c = 0; c < 4; ++c) {
-    const int vl = lane + 64 * c;
-    uint32_t pk[32];
+    const int vb = 16 * (4 * c + g);  // this group's 16 vocabulary rows
+    u32x4 pk[8];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const uint32_t lo = smem[(64 * wave + 2 * e) * GT_STRIDE + vl];
-      const uint32_t hi = smem[(64 * wave + 2 * e + 1) * GT_STRIDE + vl];
-      pk[e] = lo | (hi << 16);
+    for (int o = 0; o < 16; ++o) {  // 4-token groups of the wave's 64 tokens
+      const int tok = 64 * wave + 4 * o + sj;
+      const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(smem + tok * GT_STRIDE + vb + 4 * st));
+      pk[o >> 1][2 * (o & 1)] = (uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
+      pk[o >> 1][2 * (o & 1) + 1] = (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16);
     }
-    uint16_t* dst = a.Gt + (int64_t)(v0 + vl) * a.ldgt + j0 + 64 * wave;
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      reinterpret_cast<u32x4*>(dst)[q] = u32x4{pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]};
+    for (int h = 0; h < 2; ++h) {
+      // Groups 2h, 2h+1 stage their 32 rows; rr = staged row, piece k at slot k ^ (rr & 7).
+      if ((g >> 1) == h) {
+        const int rr = 16 * (g & 1) + i;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          *reinterpret_cast<u32x4*>(stg + rr * 128 + 16 * (k ^ (rr & 7))) = pk[k];
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rr = 8 * q + (lane >> 3), k = lane & 7;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rr * 128 + 16 * (k ^ (rr & 7)));
+        const int vrow = v0 + 64 * c + 32 * h + rr;
+        *reinterpret_cast<u32x4*>(a.Gt + (int64_t)vrow * a.ldgt + j0 + 64 * wave + 8 * k) = v;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
   }
 }
 
