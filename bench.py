@@ -100,7 +100,7 @@ def ingest_pmc(fetch_csv: str, write_csv: str) -> None:
     print(json.dumps(out, indent=1))
 
 
-def cpu_baseline(rows: int = 1536) -> dict:
+def cpu_baseline(rows: int = 2560) -> dict:
     """The fp64 oracle (as it stands) on `rows` rows of the same workload: forward + backward
     of each row, timed on this host's cores; scaled to scored tokens/s."""
     import oracle
@@ -132,7 +132,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1536)
+    ap.add_argument("--cpu-rows", type=int, default=2560)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy before the warm-up (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
