@@ -117,7 +117,7 @@ llp_status check_request(const llp_request* req) {
 
 // Workspace regions (byte offsets, each 256-byte aligned).
 struct Ws {
-  size_t count, scored, pos, tloc, tz, pm, ps, pq, G, Gt, hgT, WT, P, total;
+  size_t count, scored, pos, tloc, tz, pm, ps, pq, G, hgT, P, total;
   int64_t T_cap, nvt, ldg;
 };
 
@@ -143,9 +143,7 @@ Ws ws_layout(int64_t T, int64_t n_real, int64_t H, int op) {
     w.pq = take((size_t)(w.nvt * w.T_cap) * 4);
   } else {
     w.G = take((size_t)w.T_cap * (size_t)w.ldg * 2);    // G[j][v]
-    w.Gt = take((size_t)w.ldg * (size_t)w.T_cap * 2);   // G^T[v][j]
     w.hgT = take((size_t)H * (size_t)w.T_cap * 2);      // scored hidden rows, transposed
-    w.WT = take((size_t)H * (size_t)w.ldg * 2);         // weight, transposed
     w.P = take((size_t)DH_SPLITS * (size_t)w.T_cap * (size_t)H * 4);
   }
   w.total = off;
@@ -417,14 +415,11 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
 
   const int ntb = (int)(w.T_cap / TILE);
   uint16_t* G = at<uint16_t>(workspace, w.G);
-  uint16_t* Gt = at<uint16_t>(workspace, w.Gt);
   uint16_t* hgT = at<uint16_t>(workspace, w.hgT);
-  uint16_t* WT = at<uint16_t>(workspace, w.WT);
   float* P = at<float>(workspace, w.P);
   if (n_real > 0) {
-    // K-contiguous operand copies for the two products: the scored hidden rows transposed
-    // (hgT[h][j], zero past the count) and the weight transposed (WT[h][v], zero past the
-    // shard's real columns).
+    // The dweight product's hidden operand: the scored hidden rows transposed (hgT[h][j], zero
+    // past the count). G and the weight are read in place, K-major, by the other products.
     TransposeArgs th{};
     th.in = static_cast<const uint16_t*>(req->proj.hidden);
     th.ldi = req->proj.hidden_stride;
@@ -434,14 +429,6 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
     th.out = hgT;
     th.ldo = w.T_cap;
     LLP_HIP(launch_transpose(th, w.T_cap, s), "transpose kernel launch");
-    TransposeArgs tw{};
-    tw.in = static_cast<const uint16_t*>(req->proj.weight);
-    tw.ldi = req->proj.weight_stride;
-    tw.nvalid = n_real;
-    tw.cols = (int32_t)H;
-    tw.out = WT;
-    tw.ldo = w.ldg;
-    LLP_HIP(launch_transpose(tw, w.ldg, s), "transpose kernel launch");
 
     GradArgs ga{};
     ga.W = static_cast<const uint16_t*>(req->proj.weight);
@@ -464,15 +451,13 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
     ga.ent = in->entropy;
     ga.G = G;
     ga.ldg = w.ldg;
-    ga.Gt = Gt;
-    ga.ldgt = w.T_cap;
     LLP_HIP(launch_grad(ga, s), "gradient kernel launch");
 
     DhArgs da{};
     da.G = G;
     da.ldg = w.ldg;
-    da.WT = WT;
-    da.ldwt = w.ldg;
+    da.W = static_cast<const uint16_t*>(req->proj.weight);
+    da.ldw = req->proj.weight_stride;
     da.n_real = n_real;
     da.H = (int32_t)H;
     da.ntm = ntb;
@@ -485,7 +470,8 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
     LLP_HIP(launch_dh(da, s), "dhidden kernel launch");
 
     DwArgs wa{};
-    wa.Gt = Gt;
+    wa.G = G;
+    wa.ldg = w.ldg;
     wa.hgT = hgT;
     wa.ldk = w.T_cap;
     wa.H = (int32_t)H;

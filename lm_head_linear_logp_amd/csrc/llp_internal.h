@@ -126,15 +126,13 @@ struct GradArgs {
   const float* ent;
   uint16_t* G;
   int64_t ldg;
-  uint16_t* Gt;
-  int64_t ldgt;
 };
 
 struct DhArgs {
   const uint16_t* G;
   int64_t ldg;
-  const uint16_t* WT;
-  int64_t ldwt;
+  const uint16_t* W;  // the shard's weight rows (K-major operand of dhidden = G W)
+  int64_t ldw;
   int64_t n_real;
   int32_t H;
   int32_t ntm, ntn, nsplit, nks;
@@ -155,9 +153,10 @@ struct DhReduceArgs {
 };
 
 struct DwArgs {
-  const uint16_t* Gt;
+  const uint16_t* G;  // [scored row][local vocabulary], K-major operand of dweight = G^T hg
+  int64_t ldg;
   const uint16_t* hgT;
-  int64_t ldk;  // row stride of Gt and hgT (the scored-row capacity)
+  int64_t ldk;  // row stride of hgT (the scored-row capacity)
   int32_t H;
   int32_t ntm, ntn;
   int64_t n_real;

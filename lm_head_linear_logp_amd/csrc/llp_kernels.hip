@@ -513,68 +513,23 @@ __global__ __launch_bounds__(256) void k_topp(ToppArgs a) {
 // dhidden = G W (split over K = vocabulary in a fixed number of fixed ranges, partials
 // summed in range order) and dweight += G^T h over the scored rows in order, db += sum_j G.
 // ------------------------------------------------------------------------------------
-typedef short v4i16 __attribute__((ext_vector_type(4)));
 constexpr int GT_STRIDE = BN + 8;  // padded LDS row (bf16 elements) of the staged G tile
-constexpr int GS_BYTES = BN * GT_STRIDE * 2;
-constexpr int GT_STAGE_BYTES = 32 * 128;  // per wave: 32 rows x 64 tokens of Gt
-constexpr int GRAD_LDS_BYTES = GS_BYTES + 4 * GT_STAGE_BYTES;
+constexpr int GRAD_LDS_BYTES = BN * GT_STRIDE * 2;
 static_assert(GRAD_LDS_BYTES <= 160 * 1024, "gradient tile LDS");
 constexpr int BWDG_LDS_BYTES = GRAD_LDS_BYTES > dma::LDS_BYTES ? GRAD_LDS_BYTES : dma::LDS_BYTES;
 
-// Writes the staged bf16 tile Gs[token][vocab] (LDS) as G rows and Gt rows.
+// Writes the staged bf16 tile Gs[token][vocab] (LDS) as G rows, including the zero rows from
+// the count up to the next whole K step (the dweight product reads G K-major in steps of 64).
 __device__ __forceinline__ void grad_store(const GradArgs& a, int v0, int j0, int Ts,
                                            const uint16_t* smem) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tpad = (Ts + KSTEP - 1) / KSTEP * KSTEP;
   __syncthreads();
-  // G[j][v0 .. v0+255] for the scored rows of the tile (K = vocabulary for dhidden).
   for (int idx = threadIdx.x; idx < BN * (BM / 8); idx += NTHREADS) {
     const int tn = idx >> 5, c = idx & 31;
     const int j = j0 + tn;
-    if (j < Ts)
+    if (j < tpad)
       *reinterpret_cast<u32x4*>(a.G + (int64_t)j * a.ldg + v0 + c * 8) =
           *reinterpret_cast<const u32x4*>(smem + tn * GT_STRIDE + c * 8);
-  }
-  // Gt[v][j0 .. j0+255] (K = scored row for dweight), zeros past the count. Wave w owns tokens
-  // 64w .. 64w+63 and does 64 vocabulary rows per pass c. ds_read_b64_tr_b16 transposes within
-  // each 16-lane group: source lane 4j + t reads 4 vocabulary values (quad t) of token row j,
-  // and output lane i receives the 4 tokens' values of vocabulary column i (element i % 4 of
-  // source lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4). Lane (g, i) so collects the wave's 64 tokens
-  // of row 64c + 16g + i (128 bytes); half a pass at a time, those rows go through a per-wave
-  // LDS area (16-byte pieces XOR-swizzled by row) so that each store writes 8 whole lines.
-  const int g = lane >> 4, i = lane & 15, sj = i >> 2, st = i & 3;
-  unsigned char* stg = reinterpret_cast<unsigned char*>(const_cast<uint16_t*>(smem)) + GS_BYTES +
-                       wave * GT_STAGE_BYTES;
-#pragma unroll 1
-  for (int c = 0; c < 4; ++c) {
-    const int vb = 16 * (4 * c + g);  // this group's 16 vocabulary rows
-    u32x4 pk[8];
-#pragma unroll
-    for (int o = 0; o < 16; ++o) {  // 4-token groups of the wave's 64 tokens
-      const int tok = 64 * wave + 4 * o + sj;
-      const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4i16*)(smem + tok * GT_STRIDE + vb + 4 * st));
-      pk[o >> 1][2 * (o & 1)] = (uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
-      pk[o >> 1][2 * (o & 1) + 1] = (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // Groups 2h, 2h+1 stage their 32 rows; rr = staged row, piece k at slot k ^ (rr & 7).
-      if ((g >> 1) == h) {
-        const int rr = 16 * (g & 1) + i;
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          *reinterpret_cast<u32x4*>(stg + rr * 128 + 16 * (k ^ (rr & 7))) = pk[k];
-      }
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rr = 8 * q + (lane >> 3), k = lane & 7;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rr * 128 + 16 * (k ^ (rr & 7)));
-        const int vrow = v0 + 64 * c + 32 * h + rr;
-        *reinterpret_cast<u32x4*>(a.Gt + (int64_t)vrow * a.ldgt + j0 + 64 * wave + 8 * k) = v;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
   }
 }
 
@@ -599,7 +554,7 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArg
     de[ni] = ENT ? a.dent[row] : 0.f;
     ez[ni] = ENT ? lse - a.ent[row] : 0.f;
     tl[ni] = a.tloc[jj] - vbase;
-    // Rows past the count, and rows no gradient flows into, are exact zeros in G and Gt.
+    // Rows past the count, and rows no gradient flows into, are exact zeros in G.
     live[ni] = j < Ts && (dl[ni] != 0.f || de[ni] != 0.f);
   }
   // Stage the bf16 tile as Gs[token][vocab] in LDS, then write full rows.
@@ -667,8 +622,9 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
 #undef LLP_GRAD_EPI
 }
 
-// dhidden partials: P[split][j][n] = sum over the split's K range of G[j, k] WT[n, k]
-// (K = local vocabulary column; WT is the weight transposed, zero past the real columns).
+// dhidden partials: P[split][j][n] = sum over the split's K range of G[j, k] W[k, n]
+// (K = local vocabulary column; G is zero past the real columns, and weight rows past the
+// last real one are read as that row).
 // Tiles: grouped like the vocabulary x token grids with M = scored-row tiles.
 __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dh(DhArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
@@ -680,18 +636,17 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int Ts = *a.count;
   const int j0 = mt * BM, n0 = nt * BN;
   if (j0 >= Ts) return;
-  // G rows j0 .. j0+255 (all inside the workspace's row capacity) and WT rows n0 .. (< H).
+  // A: G rows j0 .. j0+255 (inside the workspace's row capacity), K = local vocabulary.
+  // B: the weight itself, K-major: rows = vocabulary (up to the last real one), columns
+  // n0 .. (< H).
   const int nn = a.H - n0 < BN ? a.H - n0 : BN;
   const int64_t kb = (int64_t)a.nks * dma::BKD;
-  dma::Loader la, lb;
+  dma::Loader la;
   la.init(a.G + (int64_t)j0 * a.ldg, (uint64_t)((BM - 1) * a.ldg + kb) * 2);
-  lb.init(a.WT + (int64_t)n0 * a.ldwt, (uint64_t)((nn - 1) * a.ldwt + kb) * 2);
 #pragma unroll
-  for (int u = 0; u < dma::NI; ++u) {
-    const int r = dma::Loader::row_of(u);
-    la.set(u, r, a.ldg);
-    lb.set(u, r < nn ? r : nn - 1, a.ldwt);
-  }
+  for (int u = 0; u < dma::NI; ++u) la.set(u, dma::Loader::row_of(u), a.ldg);
+  dma::LoaderK lb;
+  lb.init(a.W + n0, a.ldw, (int)a.n_real - 1, nn);
   const int ks0 = (int)((int64_t)a.nks * sp / a.nsplit);
   const int ks1 = (int)((int64_t)a.nks * (sp + 1) / a.nsplit);
   f32x16 acc[4][4];
@@ -813,8 +768,8 @@ __device__ __forceinline__ void dw_accumulate(const f32x16 (&acc)[4][4], const D
   dma::wait_vmem_le<0>();
 }
 
-// dweight[v, n] += sum_j Gt[v, j] hgT[n, j] over the scored rows j in ascending order
-// (Gt and hgT are zero past the count up to the token tile, so whole K steps can be used).
+// dweight[v, n] += sum_j G[j, v] hgT[n, j] over the scored rows j in ascending order
+// (G and hgT are zero from the count up to the next whole K step).
 __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dw(DwArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
   int mt, nt;
@@ -822,17 +777,19 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int Ts = *a.count;
   if (Ts <= 0) return;
   const int m0 = mt * BM, n0 = nt * BN;
-  // Gt rows m0 .. m0+255 (inside the padded vocabulary capacity) and hgT rows n0 .. (< H);
-  // K = scored rows rounded up to whole steps (both are zero there, up to the token tile).
+  // A: G itself, K-major: rows = scored rows (zero from the count to the next whole step),
+  // columns m0 .. m0+255 (inside the padded vocabulary capacity). B: hgT rows n0 .. (< H).
+  // K = scored rows rounded up to whole steps.
   const int nn = a.H - n0 < BN ? a.H - n0 : BN;
-  const int64_t kb = (int64_t)((Ts + dma::BKD - 1) / dma::BKD) * dma::BKD;
-  dma::Loader la, lb;
-  la.init(a.Gt + (int64_t)m0 * a.ldk, (uint64_t)((BM - 1) * a.ldk + kb) * 2);
+  const int nk = (Ts + dma::BKD - 1) / dma::BKD;
+  const int64_t kb = (int64_t)nk * dma::BKD;
+  dma::LoaderK la;
+  la.init(a.G + m0, a.ldg, (int)kb - 1, BM);
+  dma::Loader lb;
   lb.init(a.hgT + (int64_t)n0 * a.ldk, (uint64_t)((nn - 1) * a.ldk + kb) * 2);
 #pragma unroll
   for (int u = 0; u < dma::NI; ++u) {
     const int r = dma::Loader::row_of(u);
-    la.set(u, r, a.ldk);
     lb.set(u, r < nn ? r : nn - 1, a.ldk);
   }
   f32x16 acc[4][4];
@@ -843,7 +800,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
 
 // out[c][r] = in[row(r)][c] for r < nvalid (zero for nvalid <= r < the grid's rows), 64 x 64
 // bf16 tiles through LDS. row(r) = idx[r] when an index list is given, else r; nvalid is
-// *count when given. Makes hgT (gathered hidden rows, transposed) and WT (weight transposed).
+// *count when given. Makes hgT (gathered hidden rows, transposed).
 __global__ __launch_bounds__(256) void k_transpose(TransposeArgs a) {
   __shared__ uint16_t t[64][66];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;

@@ -142,29 +142,121 @@ struct Loader {
   }
 };
 
-struct Frag {
-  int aoff[4], at[4], boff[4], bt[4];
-  __device__ __forceinline__ void init(int wm, int wn, int lane) {
+// A K-major operand ([K][cols] in memory, the tile's columns contiguous): a stage holds the K
+// step's 64 rows x 256 columns, 512 bytes per K-row, and 16-byte chunk c of K-row r sits at
+// chunk c ^ fk(r). One instruction fills two K-rows; wave w fills K-rows 16w .. 16w+15 with 8
+// instructions, lane i of instruction u landing in K-row 16w + 2u + i/32 at chunk i%32.
+// The resource is rebased at every K step (its base is that step's first row), so offsets stay
+// small for any number of rows; rows past `maxrow` (the last readable one) are read as maxrow
+// and columns past the valid ones as column 0 (callers never use those values).
+__device__ __forceinline__ int fk(int r) { return 2 * (r & 3); }
+
+struct LoaderK {
+  const uint16_t* base;  // row 0, first column of the tile
+  int64_t ld;            // row stride (elements)
+  int maxrow;            // last readable row
+  int r0;                // this lane's K-row for u = 0 within a step: 16w + lane/32
+  int cb[2];             // byte offset of this lane's chunk within a K-row, by u parity
+
+  __device__ __forceinline__ void init(const uint16_t* b, int64_t ld_, int maxrow_, int ncols) {
+    base = b;
+    ld = ld_;
+    maxrow = maxrow_;
+    const int lane = threadIdx.x & 63;
+    r0 = 16 * (threadIdx.x >> 6) + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm * 128 + i * 32 + (lane & 31);
-      const int rb = wn * 128 + i * 32 + (lane & 31);
-      aoff[i] = ra * BKD;
-      at[i] = (lane >> 5) ^ swz8(ra);
-      boff[i] = rb * BKD;
-      bt[i] = (lane >> 5) ^ swz8(rb);
+    for (int p = 0; p < 2; ++p) {
+      int c = (lane & 31) ^ fk(2 * p + (lane >> 5));
+      if (8 * c >= ncols) c = 0;
+      cb[p] = 16 * c;
     }
+  }
+  __device__ __forceinline__ void issue1(uint16_t* stage, int kstep, int u) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rlim = maxrow - kstep * BKD;
+    const int r = r0 + 2 * u < rlim ? r0 + 2 * u : rlim;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + (int64_t)kstep * BKD * ld), (short)0, (int)(BKD * ld * 2), 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(stage + (16 * w + 2 * u) * BM), 16,
+        (uint32_t)(r * (int)ld * 2 + cb[u & 1]), 0, 0, 0);
   }
 };
 
-// Fragments of 16-deep substep kk (0..3): lane l holds k = 16kk + 8(l/32) + 0..7, which is
-// logical chunk 2kk + l/32 = (2kk) ^ (l/32).
-__device__ __forceinline__ void load_frag(const uint16_t* As, const uint16_t* Bs, const Frag& f,
-                                          int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+// Fragment addressing of one operand in a stage. Row-major (K-contiguous) operands read one
+// 16-byte chunk per fragment; K-major operands build it from two ds_read_b64_tr_b16, which
+// transpose within each 16-lane group: source lane 4j + t reads 4 columns (quad t) of K-row j,
+// and output lane i receives those 4 K-rows of column i (element i % 4 of source lanes i/4,
+// 4 + i/4, 8 + i/4, 12 + i/4). MFMA lane l needs column l % 32 and K = 8(l/32) + 0..7, so
+// group g = l/16 covers columns 16(g%2) .. +15 and K-rows 8(g/2) .. +7 in two reads.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+template <bool KMAJ>
+struct FragOp;
+
+template <>
+struct FragOp<false> {
+  int off[4], t[4];
+  __device__ __forceinline__ void init(int wx, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wx * 128 + i * 32 + (lane & 31);
+      off[i] = r * BKD;
+      t[i] = (lane >> 5) ^ swz8(r);
+    }
+  }
+  // The whole fragment (h must be 0).
+  __device__ __forceinline__ bf16x8 read(const uint16_t* st, int kk, int i) const {
+    return *reinterpret_cast<const bf16x8*>(st + off[i] + (((2 * kk) ^ t[i]) << 3));
+  }
+};
+
+template <>
+struct FragOp<true> {
+  int off[4];  // bytes
+  __device__ __forceinline__ void init(int wx, int lane) {
+    const int g = lane >> 4, j = (lane >> 2) & 3, t = lane & 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int chunk = wx * 16 + 4 * i + 2 * (g & 1) + (t >> 1);
+      off[i] = (8 * (g >> 1) + j) * (BM * 2) + 16 * (chunk ^ (2 * j)) + 8 * (t & 1);
+    }
+  }
+  // K-rows 16kk + 8(g/2) + 4h .. +3 of this lane's column.
+  __device__ __forceinline__ v4i16 read_half(const uint16_t* st, int kk, int i, int h) const {
+    return tr_read(reinterpret_cast<const unsigned char*>(st) + off[i] + (16 * kk + 4 * h) * (BM * 2));
+  }
+  // A restrict-qualified pointer gives the read an alias scope, so the compiler need not make
+  // it wait for DMA into the other stage.
+  static __device__ __forceinline__ v4i16 tr_read(const unsigned char* __restrict__ p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+  }
+  __device__ __forceinline__ bf16x8 read(const uint16_t* st, int kk, int i) const {
+    const v4i16 lo = read_half(st, kk, i, 0), hi = read_half(st, kk, i, 1);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
+
+template <bool AK, bool BK>
+struct Frag {
+  FragOp<AK> a;
+  FragOp<BK> b;
+  __device__ __forceinline__ void init(int wm, int wn, int lane) {
+    a.init(wm, lane);
+    b.init(wn, lane);
+  }
+};
+
+// Fragments of 16-deep substep kk (0..3): lane l holds k = 16kk + 8(l/32) + 0..7.
+template <bool AK, bool BK>
+__device__ __forceinline__ void load_frag(const uint16_t* As, const uint16_t* Bs,
+                                          const Frag<AK, BK>& f, int kk, bf16x8 (&a)[4],
+                                          bf16x8 (&b)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    a[i] = *reinterpret_cast<const bf16x8*>(As + f.aoff[i] + (((2 * kk) ^ f.at[i]) << 3));
-    b[i] = *reinterpret_cast<const bf16x8*>(Bs + f.boff[i] + (((2 * kk) ^ f.bt[i]) << 3));
+    a[i] = f.a.read(As, kk, i);
+    b[i] = f.b.read(Bs, kk, i);
   }
 }
 
@@ -198,9 +290,8 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
 
 // Issue DMA instructions LO..HI-1 of one K step (instruction i: operand i&1, slot i>>1).
-template <int LO, int HI>
-__device__ __forceinline__ void issue_range(const Loader& la, const Loader& lb, uint16_t* stage,
-                                            int kstep) {
+template <int LO, int HI, class LA, class LB>
+__device__ __forceinline__ void issue_range(const LA& la, const LB& lb, uint16_t* stage, int kstep) {
 #pragma unroll
   for (int i = LO; i < HI; ++i) {
     if (i & 1) lb.issue1(stage + STAGE, kstep, i >> 1);
@@ -208,50 +299,77 @@ __device__ __forceinline__ void issue_range(const Loader& la, const Loader& lb, 
   }
 }
 
-// Schedule of one region: 16 MFMAs, the 8 fragment reads in the first half (one per MFMA) and
-// D DMA instructions spread evenly over the 16 MFMAs.
-template <int D, int I>
+// Schedule of one region: 16 MFMAs, NR fragment reads one per MFMA from the first, and D DMA
+// instructions spread evenly over the 16 MFMAs.
+template <int D, int NR, int I>
 __device__ __forceinline__ void region_slot() {
   __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-  if constexpr (I < 8) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+  if constexpr (I < NR) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
   constexpr int nv = ((I + 1) * D) / 16 - (I * D) / 16;
   if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, nv, 0);
-  if constexpr (I + 1 < 16) region_slot<D, I + 1>();
+  if constexpr (I + 1 < 16) region_slot<D, NR, I + 1>();
 }
 
 // Memory instructions of one region in slot order (the compiler keeps LDS reads and DMA
-// writes in program order, so the source order is the issue order): slot I < 8 reads fragment
-// I/2 of A (I even) or B (I odd) for substep kk; DMA instructions QB + (I*D)/16 .. of step
-// `kstep` into `dst` follow in their slots.
-template <int D, int QB, int I>
-__device__ __forceinline__ void region_mem(const Loader& la, const Loader& lb, const uint16_t* st,
-                                           const Frag& f, int kk, bf16x8 (&na)[4],
-                                           bf16x8 (&nb)[4], uint16_t* dst, int kstep) {
-  if constexpr (I < 8) {
-    constexpr int i = I >> 1;
-    if constexpr (I & 1)
-      nb[i] = *reinterpret_cast<const bf16x8*>(st + STAGE + f.boff[i] + (((2 * kk) ^ f.bt[i]) << 3));
-    else
-      na[i] = *reinterpret_cast<const bf16x8*>(st + f.aoff[i] + (((2 * kk) ^ f.at[i]) << 3));
+// writes in program order, so the source order is the issue order). Reads go fragment by
+// fragment, A then B, one or two reads each (row-major or K-major); DMA instructions
+// QB + (I*D)/16 .. of step `kstep` into `dst` follow in their slots.
+template <bool AK, bool BK>
+struct ReadPlan {
+  static constexpr int RA = AK ? 2 : 1, RB = BK ? 2 : 1, PER = RA + RB, NR = 4 * PER;
+};
+
+template <int D, int QB, int I, bool AK, bool BK, class LA, class LB>
+__device__ __forceinline__ void region_mem(const LA& la, const LB& lb, const uint16_t* st,
+                                           const Frag<AK, BK>& f, int kk, bf16x8 (&na)[4],
+                                           bf16x8 (&nb)[4], v4i16 (&tmp)[4], uint16_t* dst,
+                                           int kstep) {
+  using P = ReadPlan<AK, BK>;
+  if constexpr (I < P::NR) {
+    constexpr int i = I / P::PER, r = I % P::PER;
+    if constexpr (r < P::RA) {
+      if constexpr (!AK) {
+        na[i] = f.a.read(st, kk, i);
+      } else if constexpr (r == 0) {
+        tmp[i] = f.a.read_half(st, kk, i, 0);
+      } else {
+        const v4i16 hi = f.a.read_half(st, kk, i, 1);
+        na[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tmp[i], hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    } else {
+      constexpr int rb = r - P::RA;
+      if constexpr (!BK) {
+        nb[i] = f.b.read(st + STAGE, kk, i);
+      } else if constexpr (rb == 0) {
+        tmp[i] = f.b.read_half(st + STAGE, kk, i, 0);
+      } else {
+        const v4i16 hi = f.b.read_half(st + STAGE, kk, i, 1);
+        nb[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tmp[i], hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
   }
   issue_range<QB + (I * D) / 16, QB + ((I + 1) * D) / 16>(la, lb, dst, kstep);
-  if constexpr (I + 1 < 16) region_mem<D, QB, I + 1>(la, lb, st, f, kk, na, nb, dst, kstep);
+  if constexpr (I + 1 < 16)
+    region_mem<D, QB, I + 1, AK, BK>(la, lb, st, f, kk, na, nb, tmp, dst, kstep);
 }
 
 // One region: 16 MFMAs on (a, b); fragment reads of substep kk from stage `st` into (na, nb);
 // DMA instructions QB .. QB+D-1 of step `kstep` into stage `dst`.
-template <int D, int QB>
-__device__ __forceinline__ void region(const Loader& la, const Loader& lb, const bf16x8 (&a)[4],
-                                       const bf16x8 (&b)[4], const uint16_t* st, const Frag& f,
-                                       int kk, bf16x8 (&na)[4], bf16x8 (&nb)[4], uint16_t* dst,
-                                       int kstep, f32x16 (&acc)[4][4]) {
+template <int D, int QB, bool AK, bool BK, class LA, class LB>
+__device__ __forceinline__ void region(const LA& la, const LB& lb, const bf16x8 (&a)[4],
+                                       const bf16x8 (&b)[4], const uint16_t* st,
+                                       const Frag<AK, BK>& f, int kk, bf16x8 (&na)[4],
+                                       bf16x8 (&nb)[4], uint16_t* dst, int kstep,
+                                       f32x16 (&acc)[4][4]) {
+  v4i16 tmp[4];
   mfmas<0, 16>(a, b, acc);
-  region_mem<D, QB, 0>(la, lb, st, f, kk, na, nb, dst, kstep);
-  region_slot<D, 0>();
+  region_mem<D, QB, 0, AK, BK>(la, lb, st, f, kk, na, nb, tmp, dst, kstep);
+  region_slot<D, ReadPlan<AK, BK>::NR, 0>();
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// acc += A[M-tile, K-steps ks0..ks1) . B[N-tile, same]^T in ascending K order.
+// acc += A[M-tile, K-steps ks0..ks1) . B[N-tile, same]^T in ascending K order. LA/LB are Loader
+// (row-major, K-contiguous) or LoaderK (K-major); the fragment layout follows.
 // Step s (stage s%2) runs four 16-deep substeps in four branch-free regions; fragments
 // alternate between two register sets and each region reads the next substep's:
 //   R1:     MFMAs of kk0, reads of kk1, DMA of step s+1 (its last 8 loads)
@@ -259,16 +377,19 @@ __device__ __forceinline__ void region(const Loader& la, const Loader& lb, const
 //   -- wait for step s+1's DMA, barrier (every wave is done reading stage s%2) --
 //   R4:     MFMAs of kk3, reads of kk0 of step s+1, DMA of step s+2 (its first 8 loads)
 // A step's 16 loads are split over two regions, one per two MFMAs: issued in one burst they
-// back up the address unit, and the in-order issue stalls the MFMAs queued behind them. DMA steps past
-// the end are clamped to the last step (an in-bounds reload into a stage that is never read
-// again), which keeps every iteration the same shape. All DMA is drained before returning.
-__device__ __forceinline__ void mainloop(const Loader& la, const Loader& lb, int ks0, int ks1,
+// back up the address unit, and the in-order issue stalls the MFMAs queued behind them. DMA
+// steps past the end are clamped to the last step (an in-bounds reload into a stage that is
+// never read again), which keeps every iteration the same shape. All DMA is drained before
+// returning.
+template <class LA, class LB>
+__device__ __forceinline__ void mainloop(const LA& la, const LB& lb, int ks0, int ks1,
                                          uint16_t* smem, f32x16 (&acc)[4][4]) {
+  constexpr bool AK = !__is_same(LA, Loader), BK = !__is_same(LB, Loader);
   constexpr int NQ = 2 * NI, Q4 = NI, Q1 = NI;  // loads per step: 8 in R4, 8 in R1
   const int n = ks1 - ks0;
   if (n <= 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  Frag f;
+  Frag<AK, BK> f;
   f.init(wave & 1, wave >> 1, lane);
   const int k1 = ks0 + (1 < n ? 1 : 0);
   issue_range<0, NQ>(la, lb, smem, ks0);
