@@ -277,3 +277,87 @@ def top_p_replay(logits_rows, replay_ids, targets, temperature: float, offset: i
         else:
             out["logp"][t] = NEG_INF
     return out
+
+
+def logits_forward(logits_rows, targets, temperature: float, offset: int, local_size: int,
+                   real_vocab: int, mask=None, world: int = 1) -> dict:
+    """Per-shard partials from the shard's precomputed local logits.
+
+    [CUDA provider, "Megatron integration"]: strict LM-head local logits are reused when
+    available, with no second projection. [top-p replay, "Summary"]: temperature scaling
+    happens once, so the given logits are the unscaled h . W^T + b and z = x / tau here.
+    ``logits_rows`` is [T, local_size] (fp32 numbers or bf16 bit patterns); only the first
+    clamp(real_vocab - offset, 0, local_size) columns are part of the distribution. The
+    outputs are those of ``shard_forward``; with world == 1 a target outside the real range
+    also sets the not-found bit, as there is no other shard to hold it.
+    """
+    x = as_f64(logits_rows)
+    T = x.shape[0]
+    targets = np.asarray(targets, dtype=np.int64)
+    mask = np.ones(T, dtype=bool) if mask is None else np.asarray(mask).astype(bool)
+    n_real = int(min(max(real_vocab - offset, 0), local_size))
+    out = dict(target_logit=np.zeros(T), in_range=np.zeros(T, dtype=np.uint8),
+               lse=np.zeros(T), entropy=np.zeros(T), logp=np.zeros(T), status=0)
+    rows = np.nonzero(mask)[0]
+    if rows.size == 0:
+        return out
+    if np.any((targets[rows] < 0) | (targets[rows] >= real_vocab)):
+        out["status"] |= ST_TARGET_OUT_OF_RANGE
+    z = x[rows][:, :n_real] / temperature
+    lse, ent = softmax_stats(z)
+    loc = targets[rows] - offset
+    hit = (loc >= 0) & (loc < n_real) & (targets[rows] < real_vocab)
+    t = np.zeros(rows.size)
+    t[hit] = z[np.nonzero(hit)[0], loc[hit]]
+    out["target_logit"][rows] = t
+    out["in_range"][rows] = hit.astype(np.uint8)
+    out["lse"][rows] = lse
+    out["entropy"][rows] = ent
+    out["logp"][rows] = np.where(hit, t - lse, NEG_INF)
+    if world == 1 and np.any(~hit):
+        out["status"] |= ST_TARGET_NOT_FOUND
+    return out
+
+
+def keep_mask_replay(logits_rows, keep_mask, targets, temperature: float, offset: int,
+                     local_size: int, real_vocab: int, mask=None) -> dict:
+    """Dense keep-mask replay scoring of one shard.
+
+    [top-p replay, "Changes" table, VIME masked replay behavior]: the local logits are reused
+    with a keep mask and excluded entries are -inf, so per row U = the kept local columns
+    among the shard's real ones and lse_N = log sum_{v in U} exp(x_v / tau); the target logit
+    is x_tgt / tau when the target is kept. [top-p replay, "Validation"]: this dense form and
+    the compact replay of the same nucleus give the same results. ``keep_mask`` is
+    [T, local_size] with nonzero = kept.
+    """
+    x = as_f64(logits_rows)
+    km = np.asarray(keep_mask)
+    T = x.shape[0]
+    targets = np.asarray(targets, dtype=np.int64)
+    mask = np.ones(T, bool) if mask is None else np.asarray(mask).astype(bool)
+    n_real = int(min(max(real_vocab - offset, 0), local_size))
+    out = dict(target_logit=np.zeros(T), in_range=np.zeros(T, dtype=np.uint8),
+               lse=np.zeros(T), logp=np.zeros(T), status=0)
+    for t in range(T):
+        if not mask[t]:
+            continue
+        if targets[t] < 0 or targets[t] >= real_vocab:
+            out["status"] |= ST_TARGET_OUT_OF_RANGE
+        cols = np.nonzero(km[t, :n_real])[0]
+        if cols.size == 0:
+            out["lse"][t] = NEG_INF
+            out["logp"][t] = NEG_INF
+            continue
+        z = x[t, cols] / temperature
+        m = z.max()
+        lse = m + np.log(np.exp(z - m).sum())
+        out["lse"][t] = lse
+        loc = int(targets[t]) - offset
+        if 0 <= loc < n_real and km[t, loc] and targets[t] < real_vocab:
+            tz = x[t, loc] / temperature
+            out["target_logit"][t] = tz
+            out["in_range"][t] = 1
+            out["logp"][t] = tz - lse
+        else:
+            out["logp"][t] = NEG_INF
+    return out
