@@ -247,6 +247,53 @@ typedef struct {
   int32_t* status_word;
 } llp_topp_request;
 
+/* Logits-input forward request ([CUDA provider, "Megatron integration"]: strict LM-head local
+ * logits are reused when available, avoiding a second projection; [top-p replay, "Summary"]:
+ * temperature is applied exactly once).
+ *   logits        [T, local_size] of logits_dtype (LLP_DTYPE_F32 or LLP_DTYPE_BF16), the
+ *                 shard's unscaled local logits h . W^T + b; row stride logits_stride
+ *                 (elements, >= local_size; the rows must be 16-byte aligned: base aligned and
+ *                 stride * element size a multiple of 16). Padded columns are never read.
+ *   vocab, layout, target_ids, temperature, flags, status_word: as in llp_request (z = x *
+ *                 fl32(1/temperature); flags: LLP_FLAG_WANT_ENTROPY). */
+typedef struct {
+  const void* logits;
+  int32_t logits_dtype;
+  int32_t reserved;
+  int64_t logits_stride;
+  llp_vocab_partition vocab;
+  llp_token_layout layout;
+  const int64_t* target_ids;
+  float temperature;
+  uint32_t flags;
+  int32_t* status_word;
+} llp_logits_request;
+
+/* Dense keep-mask replay request ([top-p replay, "Changes" table]: the local logits are
+ * reused with a keep mask and excluded entries are -inf; [top-p replay, "Validation"]: the
+ * dense-mask and compact forms agree bitwise across shard offsets and empty shards).
+ *   logits        as in llp_topp_request, with 16-byte aligned rows (see llp_logits_request).
+ *   keep_mask     uint8 [num_tokens, local_size], row stride keep_stride (bytes, >= local_size,
+ *                 multiple of 16), 16-byte aligned base; nonzero = the column is in the row's
+ *                 nucleus. Columns past the shard's real ones are ignored.
+ *   num_tokens, vocab, target_ids, loss_mask, temperature, processed_logprobs, status_word:
+ *                 as in llp_topp_request. */
+typedef struct {
+  const void* logits;
+  int32_t logits_dtype;
+  int32_t processed_logprobs;
+  int64_t logits_stride;
+  const uint8_t* keep_mask;
+  int64_t keep_stride;
+  int64_t num_tokens;
+  llp_vocab_partition vocab;
+  const int64_t* target_ids;
+  const uint8_t* loss_mask;
+  float temperature;
+  int32_t reserved;
+  int32_t* status_word;
+} llp_keep_mask_request;
+
 /* Loading phase: checks that `device` is a gfx950 GPU and loads the kernels on it; fills
  * `info` (may be NULL). Returns LLP_ERR_UNAVAILABLE when there is no such device. Must
  * succeed on the current device before any execution call. Idempotent. */
@@ -287,6 +334,18 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
  * over the shards for the final log-probability. */
 LLP_API llp_status llp_top_p_replay(const llp_topp_request* req, const llp_partials* out,
                                     void* stream);
+
+/* Logits-input forward for one shard: the partials of llp_forward (target_logit, in_range,
+ * lse required; entropy with LLP_FLAG_WANT_ENTROPY; logp optional) from the shard's local
+ * logits instead of hidden states and weight. Needs no workspace. */
+LLP_API llp_status llp_forward_logits(const llp_logits_request* req, const llp_partials* out,
+                                      void* stream);
+
+/* Dense keep-mask replay scoring for one shard: the partials of llp_top_p_replay (entropy must
+ * be NULL) for the nucleus given as a keep mask. For a nucleus of at most LLP_MAX_REPLAY_IDS
+ * ids the results are bitwise those of llp_top_p_replay given the same ids. */
+LLP_API llp_status llp_keep_mask_replay(const llp_keep_mask_request* req,
+                                        const llp_partials* out, void* stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 LLP_API const char* llp_last_error(void);

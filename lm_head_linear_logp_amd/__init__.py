@@ -17,7 +17,7 @@ import torch
 from . import _capi as A
 
 __all__ = ["LLPError", "open", "workspace_bytes", "forward", "merge", "backward",
-           "top_p_replay", "last_error", "STATUS_BITS"]
+           "top_p_replay", "last_error", "STATUS_BITS", "forward_logits", "keep_mask_replay"]
 
 STATUS_BITS = {"TARGET_OUT_OF_RANGE": A.LLP_STATUS_TARGET_OUT_OF_RANGE,
                "TARGET_NOT_FOUND": A.LLP_STATUS_TARGET_NOT_FOUND,
@@ -304,4 +304,117 @@ def top_p_replay(logits: torch.Tensor, replay_ids: torch.Tensor, target_ids: tor
                        _ptr(out["logp"]))
     _check(A.load().llp_top_p_replay(C.byref(req), C.byref(o), _stream_ptr(dev)),
            "llp_top_p_replay")
+    return out
+
+
+def _vocab(req_vocab, offset, local_size, real_vocab, padded_vocab, rank, world):
+    if padded_vocab is None:
+        padded_vocab = local_size if world == 1 else None
+    if real_vocab is None:
+        real_vocab = padded_vocab
+    if padded_vocab is None:
+        raise ValueError("padded_vocab is required for a vocabulary shard (world > 1)")
+    req_vocab.offset = int(offset)
+    req_vocab.local_size = int(local_size)
+    req_vocab.real_vocab = int(real_vocab)
+    req_vocab.padded_vocab = int(padded_vocab)
+    req_vocab.rank = int(rank)
+    req_vocab.world = int(world)
+
+
+def _logits_view(logits, local_size):
+    if logits.dtype not in (torch.float32, torch.bfloat16) or logits.dim() != 2:
+        raise TypeError("logits must be a 2-d fp32 or bf16 tensor")
+    if logits.stride(1) != 1:
+        raise ValueError("logits must be contiguous in its last dimension")
+    dt = A.LLP_DTYPE_F32 if logits.dtype == torch.float32 else A.LLP_DTYPE_BF16
+    return dt, (logits.stride(0) if logits.shape[0] > 0 else local_size)
+
+
+def forward_logits(logits: torch.Tensor, target_ids: torch.Tensor, *, temperature: float,
+                   loss_mask: Optional[torch.Tensor] = None,
+                   cu_seqlens: Optional[torch.Tensor] = None, offset: int = 0,
+                   real_vocab: Optional[int] = None, padded_vocab: Optional[int] = None,
+                   rank: int = 0, world: int = 1, want_entropy: bool = True,
+                   status: Optional[torch.Tensor] = None,
+                   local_size: Optional[int] = None) -> dict:
+    """llp_forward_logits on one shard's unscaled local logits [T, local_size] (fp32 or bf16;
+    a strided view of a wider tensor is fine). Returns the partials of ``forward``."""
+    dev = logits.device
+    open(dev.index)
+    _need(target_ids, "target_ids", torch.int64, 1, dev)
+    T = target_ids.shape[0]
+    if local_size is None:
+        local_size = logits.shape[1]
+    req = A.llp_logits_request()
+    req.logits = _ptr(logits)
+    req.logits_dtype, req.logits_stride = _logits_view(logits, local_size)
+    _vocab(req.vocab, offset, local_size, real_vocab, padded_vocab, rank, world)
+    req.layout.num_tokens = T
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+        req.layout.cu_seqlens = _ptr(cu_seqlens)
+        req.layout.num_seqs = cu_seqlens.shape[0] - 1
+    if loss_mask is not None:
+        _need(loss_mask, "loss_mask", torch.uint8, 1, dev)
+        req.layout.loss_mask = _ptr(loss_mask)
+    req.target_ids = _ptr(target_ids)
+    req.temperature = float(temperature)
+    req.flags = A.LLP_FLAG_WANT_ENTROPY if want_entropy else 0
+    if status is not None:
+        _need(status, "status", torch.int32, 1, dev)
+        req.status_word = _ptr(status)
+    out = dict(target_logit=torch.empty(T, dtype=torch.float32, device=dev),
+               in_range=torch.empty(T, dtype=torch.uint8, device=dev),
+               lse=torch.empty(T, dtype=torch.float32, device=dev),
+               entropy=torch.empty(T, dtype=torch.float32, device=dev) if want_entropy else None,
+               logp=torch.empty(T, dtype=torch.float32, device=dev))
+    o = A.llp_partials(_ptr(out["target_logit"]), _ptr(out["in_range"]), _ptr(out["lse"]),
+                       _ptr(out["entropy"]), _ptr(out["logp"]))
+    _check(A.load().llp_forward_logits(C.byref(req), C.byref(o), _stream_ptr(dev)),
+           "llp_forward_logits")
+    return out
+
+
+def keep_mask_replay(logits: torch.Tensor, keep_mask: torch.Tensor, target_ids: torch.Tensor, *,
+                     temperature: float, offset: int = 0, real_vocab: Optional[int] = None,
+                     padded_vocab: Optional[int] = None, rank: int = 0, world: int = 1,
+                     loss_mask: Optional[torch.Tensor] = None, processed_logprobs: bool = True,
+                     status: Optional[torch.Tensor] = None,
+                     local_size: Optional[int] = None) -> dict:
+    """llp_keep_mask_replay on one shard: local logits [T, local_size] and a uint8 keep mask of
+    the same shape (views of wider tensors are fine). Returns target_logit, in_range, lse,
+    logp, as ``top_p_replay``."""
+    dev = logits.device
+    open(dev.index)
+    _need(target_ids, "target_ids", torch.int64, 1, dev)
+    if keep_mask.dtype != torch.uint8 or keep_mask.dim() != 2 or keep_mask.stride(1) != 1:
+        raise TypeError("keep_mask must be a 2-d uint8 tensor contiguous in its last dimension")
+    T = target_ids.shape[0]
+    if local_size is None:
+        local_size = logits.shape[1]
+    req = A.llp_keep_mask_request()
+    req.logits = _ptr(logits)
+    req.logits_dtype, req.logits_stride = _logits_view(logits, local_size)
+    req.keep_mask = _ptr(keep_mask)
+    req.keep_stride = keep_mask.stride(0) if keep_mask.shape[0] > 0 else local_size
+    req.num_tokens = T
+    _vocab(req.vocab, offset, local_size, real_vocab, padded_vocab, rank, world)
+    req.target_ids = _ptr(target_ids)
+    if loss_mask is not None:
+        _need(loss_mask, "loss_mask", torch.uint8, 1, dev)
+        req.loss_mask = _ptr(loss_mask)
+    req.temperature = float(temperature)
+    req.processed_logprobs = 1 if processed_logprobs else 0
+    if status is not None:
+        _need(status, "status", torch.int32, 1, dev)
+        req.status_word = _ptr(status)
+    out = dict(target_logit=torch.empty(T, dtype=torch.float32, device=dev),
+               in_range=torch.empty(T, dtype=torch.uint8, device=dev),
+               lse=torch.empty(T, dtype=torch.float32, device=dev),
+               logp=torch.empty(T, dtype=torch.float32, device=dev))
+    o = A.llp_partials(_ptr(out["target_logit"]), _ptr(out["in_range"]), _ptr(out["lse"]), None,
+                       _ptr(out["logp"]))
+    _check(A.load().llp_keep_mask_replay(C.byref(req), C.byref(o), _stream_ptr(dev)),
+           "llp_keep_mask_replay")
     return out

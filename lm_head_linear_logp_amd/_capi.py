@@ -83,6 +83,21 @@ class llp_topp_request(C.Structure):
                 ("processed_logprobs", C.c_int32), ("status_word", vp)]
 
 
+class llp_logits_request(C.Structure):
+    _fields_ = [("logits", vp), ("logits_dtype", C.c_int32), ("reserved", C.c_int32),
+                ("logits_stride", C.c_int64), ("vocab", llp_vocab_partition),
+                ("layout", llp_token_layout), ("target_ids", vp), ("temperature", C.c_float),
+                ("flags", C.c_uint32), ("status_word", vp)]
+
+
+class llp_keep_mask_request(C.Structure):
+    _fields_ = [("logits", vp), ("logits_dtype", C.c_int32), ("processed_logprobs", C.c_int32),
+                ("logits_stride", C.c_int64), ("keep_mask", vp), ("keep_stride", C.c_int64),
+                ("num_tokens", C.c_int64), ("vocab", llp_vocab_partition), ("target_ids", vp),
+                ("loss_mask", vp), ("temperature", C.c_float), ("reserved", C.c_int32),
+                ("status_word", vp)]
+
+
 SIGNATURES = {
     "llp_open": (C.c_int, [C.c_int32, C.POINTER(llp_info)]),
     "llp_workspace_bytes": (C.c_int, [C.POINTER(llp_request), C.c_int32, C.POINTER(C.c_size_t)]),
@@ -92,6 +107,9 @@ SIGNATURES = {
     "llp_backward": (C.c_int, [C.POINTER(llp_request), C.POINTER(llp_bwd_in),
                                C.POINTER(llp_bwd_out), vp, C.c_size_t, vp]),
     "llp_top_p_replay": (C.c_int, [C.POINTER(llp_topp_request), C.POINTER(llp_partials), vp]),
+    "llp_forward_logits": (C.c_int, [C.POINTER(llp_logits_request), C.POINTER(llp_partials), vp]),
+    "llp_keep_mask_replay": (C.c_int, [C.POINTER(llp_keep_mask_request), C.POINTER(llp_partials),
+                                       vp]),
     "llp_last_error": (C.c_char_p, []),
 }
 

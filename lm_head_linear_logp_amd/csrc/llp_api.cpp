@@ -179,6 +179,123 @@ T* at(void* ws, size_t off) {
 
 extern "C" {
 
+// Rows of a logits view are read with 16-byte loads.
+static bool rows_aligned(const void* p, int64_t stride, int64_t esize) {
+  return p == nullptr || (aligned(p, 16) && (stride * esize) % 16 == 0);
+}
+
+LLP_API llp_status llp_forward_logits(const llp_logits_request* req, const llp_partials* out,
+                                      void* stream) {
+  LLP_CHECK(req != nullptr && out != nullptr, LLP_ERR_INVALID_ARGUMENT, "req/out is NULL");
+  llp_status st = check_partition(req->vocab);
+  if (st != LLP_OK) return st;
+  const int64_t T = req->layout.num_tokens;
+  LLP_CHECK(T >= 0 && T < (int64_t(1) << 31), LLP_ERR_INVALID_ARGUMENT, "num_tokens out of range");
+  LLP_CHECK(req->logits_dtype == LLP_DTYPE_F32 || req->logits_dtype == LLP_DTYPE_BF16,
+            LLP_ERR_INVALID_ARGUMENT, "logits_dtype %d is not F32 or BF16", req->logits_dtype);
+  const int64_t esize = req->logits_dtype == LLP_DTYPE_F32 ? 4 : 2;
+  LLP_CHECK(req->logits_stride >= req->vocab.local_size, LLP_ERR_INVALID_ARGUMENT,
+            "logits_stride < local_size");
+  LLP_CHECK(rows_aligned(req->logits, req->logits_stride, esize), LLP_ERR_INVALID_ARGUMENT,
+            "logits rows must be 16-byte aligned (base and stride * element size)");
+  LLP_CHECK(isfinite(req->temperature) && req->temperature > 0.f, LLP_ERR_INVALID_ARGUMENT,
+            "temperature must be finite and > 0");
+  LLP_CHECK((req->flags & ~uint32_t(LLP_FLAG_WANT_ENTROPY)) == 0, LLP_ERR_INVALID_ARGUMENT,
+            "unknown flags 0x%x", req->flags);
+  if (req->layout.cu_seqlens != nullptr)
+    LLP_CHECK(req->layout.num_seqs >= 0, LLP_ERR_INVALID_ARGUMENT, "num_seqs < 0");
+  if (T > 0) {
+    LLP_CHECK(req->target_ids != nullptr, LLP_ERR_INVALID_ARGUMENT, "target_ids is NULL");
+    LLP_CHECK(req->logits || local_real(req->vocab) == 0, LLP_ERR_INVALID_ARGUMENT,
+              "logits is NULL");
+    LLP_CHECK(out->target_logit && out->in_range && out->lse, LLP_ERR_INVALID_ARGUMENT,
+              "out.target_logit, out.in_range and out.lse are required");
+    LLP_CHECK(((req->flags & LLP_FLAG_WANT_ENTROPY) != 0) == (out->entropy != nullptr),
+              LLP_ERR_INVALID_ARGUMENT, "out.entropy must be given exactly when entropy is wanted");
+  }
+  st = check_device();
+  if (st != LLP_OK) return st;
+  if (T == 0) return LLP_OK;
+  LogitsArgs la{};
+  la.T = T;
+  la.logits = req->logits;
+  la.bf16 = req->logits_dtype == LLP_DTYPE_BF16;
+  la.ld = req->logits_stride;
+  la.offset = req->vocab.offset;
+  la.n_real = local_real(req->vocab);
+  la.real_vocab = req->vocab.real_vocab;
+  la.world = req->vocab.world;
+  la.mask = req->layout.loss_mask;
+  la.cu_seqlens = req->layout.cu_seqlens;
+  la.num_seqs = req->layout.num_seqs;
+  la.targets = req->target_ids;
+  la.c1 = (float)(1.0 / (double)req->temperature);
+  la.out_t = out->target_logit;
+  la.out_f = out->in_range;
+  la.out_l = out->lse;
+  la.out_e = out->entropy;
+  la.out_p = out->logp;
+  la.status = req->status_word;
+  LLP_HIP(launch_logits(la, static_cast<hipStream_t>(stream)), "logits forward kernel launch");
+  return LLP_OK;
+}
+
+LLP_API llp_status llp_keep_mask_replay(const llp_keep_mask_request* req,
+                                        const llp_partials* out, void* stream) {
+  LLP_CHECK(req != nullptr && out != nullptr, LLP_ERR_INVALID_ARGUMENT, "req/out is NULL");
+  llp_status st = check_partition(req->vocab);
+  if (st != LLP_OK) return st;
+  const int64_t T = req->num_tokens;
+  LLP_CHECK(T >= 0 && T < (int64_t(1) << 40), LLP_ERR_INVALID_ARGUMENT, "num_tokens out of range");
+  LLP_CHECK(req->processed_logprobs == 1, LLP_ERR_INVALID_ARGUMENT,
+            "replay scores processed logprobs only (processed_logprobs must be 1)");
+  LLP_CHECK(req->logits_dtype == LLP_DTYPE_F32 || req->logits_dtype == LLP_DTYPE_BF16,
+            LLP_ERR_INVALID_ARGUMENT, "logits_dtype %d is not F32 or BF16", req->logits_dtype);
+  const int64_t esize = req->logits_dtype == LLP_DTYPE_F32 ? 4 : 2;
+  LLP_CHECK(req->logits_stride >= req->vocab.local_size, LLP_ERR_INVALID_ARGUMENT,
+            "logits_stride < local_size");
+  LLP_CHECK(rows_aligned(req->logits, req->logits_stride, esize), LLP_ERR_INVALID_ARGUMENT,
+            "logits rows must be 16-byte aligned (base and stride * element size)");
+  LLP_CHECK(req->keep_stride >= req->vocab.local_size, LLP_ERR_INVALID_ARGUMENT,
+            "keep_stride < local_size");
+  LLP_CHECK(rows_aligned(req->keep_mask, req->keep_stride, 1), LLP_ERR_INVALID_ARGUMENT,
+            "keep_mask rows must be 16-byte aligned (base and stride)");
+  LLP_CHECK(isfinite(req->temperature) && req->temperature > 0.f, LLP_ERR_INVALID_ARGUMENT,
+            "temperature must be finite and > 0");
+  LLP_CHECK(out->entropy == nullptr, LLP_ERR_INVALID_ARGUMENT,
+            "replay produces no entropy (out.entropy must be NULL)");
+  if (T > 0) {
+    LLP_CHECK(req->target_ids != nullptr, LLP_ERR_INVALID_ARGUMENT, "target_ids is NULL");
+    LLP_CHECK((req->logits && req->keep_mask) || local_real(req->vocab) == 0,
+              LLP_ERR_INVALID_ARGUMENT, "logits and keep_mask are required");
+    LLP_CHECK(out->target_logit && out->in_range && out->lse, LLP_ERR_INVALID_ARGUMENT,
+              "out.target_logit, out.in_range and out.lse are required");
+  }
+  st = check_device();
+  if (st != LLP_OK) return st;
+  if (T == 0) return LLP_OK;
+  KeepArgs ka{};
+  ka.T = T;
+  ka.logits = req->logits;
+  ka.bf16 = req->logits_dtype == LLP_DTYPE_BF16;
+  ka.lstride = req->logits_stride;
+  ka.keep = req->keep_mask;
+  ka.kstride = req->keep_stride;
+  ka.offset = req->vocab.offset;
+  ka.n_real = local_real(req->vocab);
+  ka.real_vocab = req->vocab.real_vocab;
+  ka.mask = req->loss_mask;
+  ka.targets = req->target_ids;
+  ka.c1 = (float)(1.0 / (double)req->temperature);
+  ka.out_t = out->target_logit;
+  ka.out_f = out->in_range;
+  ka.out_l = out->lse;
+  ka.out_p = out->logp;
+  ka.status = req->status_word;
+  LLP_HIP(launch_keep(ka, static_cast<hipStream_t>(stream)), "keep-mask replay kernel launch");
+  return LLP_OK;
+}
+
 LLP_API const char* llp_last_error(void) { return g_err; }
 
 LLP_API llp_status llp_open(int32_t device, llp_info* info) {

@@ -106,6 +106,44 @@ struct ToppArgs {
   int32_t* status;
 };
 
+struct LogitsArgs {
+  int64_t T;
+  const void* logits;
+  int32_t bf16;
+  int64_t ld;
+  int64_t offset, n_real, real_vocab;
+  int32_t world;
+  const uint8_t* mask;
+  const int32_t* cu_seqlens;
+  int32_t num_seqs;
+  const int64_t* targets;
+  float c1;
+  float* out_t;
+  uint8_t* out_f;
+  float* out_l;
+  float* out_e;
+  float* out_p;
+  int32_t* status;
+};
+
+struct KeepArgs {
+  int64_t T;
+  const void* logits;
+  int32_t bf16;
+  int64_t lstride;
+  const uint8_t* keep;
+  int64_t kstride;
+  int64_t offset, n_real, real_vocab;
+  const uint8_t* mask;
+  const int64_t* targets;
+  float c1;
+  float* out_t;
+  uint8_t* out_f;
+  float* out_l;
+  float* out_p;
+  int32_t* status;
+};
+
 struct GradArgs {
   const uint16_t* W;
   int64_t ldw;
@@ -195,6 +233,8 @@ hipError_t launch_dh_reduce(const DhReduceArgs& a, hipStream_t s);
 hipError_t launch_dw(const DwArgs& a, hipStream_t s);
 hipError_t launch_transpose(const TransposeArgs& a, int64_t rows, hipStream_t s);
 hipError_t launch_dbias(const DbArgs& a, hipStream_t s);
+hipError_t launch_logits(const LogitsArgs& a, hipStream_t s);
+hipError_t launch_keep(const KeepArgs& a, hipStream_t s);
 hipError_t probe_kernels();
 
 }  // namespace llp

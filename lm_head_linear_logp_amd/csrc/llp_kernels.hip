@@ -414,6 +414,20 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
 // i-th distinct id on lane i, so the fixed butterfly sum is independent of the order and
 // multiplicity of the listed ids.
 // ------------------------------------------------------------------------------------
+// Scores a set of logits held one per lane in ascending-id order (lane i holds the i-th
+// distinct id's z when `live`, else -inf): M = max, returns sum exp(z - M), both by a fixed
+// butterfly, so the result is a function of the set alone. The compact and the dense
+// keep-mask scorers both end here, which makes them bitwise equal on the same nucleus.
+__device__ __forceinline__ float wave_set_sum(float z, bool live, float& M) {
+  M = z;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float e = live ? expf(z - M) : 0.f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) e += __shfl_xor(e, off);
+  return e;
+}
+
 __global__ __launch_bounds__(256) void k_topp(ToppArgs a) {
   __shared__ float zs[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -471,13 +485,8 @@ __global__ __launch_bounds__(256) void k_topp(ToppArgs a) {
   const uint64_t tb = __builtin_amdgcn_ballot_w64(has_t);
   // zs[w] is private to this wave; one wave's LDS accesses complete in issue order.
   __builtin_amdgcn_wave_barrier();
-  const float z = lane < n ? zs[w][lane] : -INFINITY;
-  float M = z;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float e = lane < n ? expf(z - M) : 0.f;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) e += __shfl_xor(e, off);
+  float M;
+  const float e = wave_set_sum(lane < n ? zs[w][lane] : -INFINITY, lane < n, M);
   if (lane == 0) {
     if (n == 0) {
       a.out_t[row] = 0.f;
@@ -848,6 +857,241 @@ __global__ __launch_bounds__(256) void k_dbias(DbArgs a) {
 // ------------------------------------------------------------------------------------
 static inline int ceil_div64(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// ------------------------------------------------------------------------------------
+// Logits-input forward ([CUDA provider, "Megatron integration"]: reuse the LM head's local
+// logits, no second projection). One workgroup per row streams the row's real columns once:
+// each thread keeps a running (m, s, q) with s = sum 2^d, q = sum 2^d d, d = (z - m) log2 e,
+// z = x * fl32(1/tau), over 8 columns at a time (rescaled when a chunk raises m); the 256
+// partials are folded in a fixed order (lanes by halving strides, then waves 0..3) with the
+// tile combine's algebra. Outputs and status bits as llp_forward's.
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ void load8(const void* base, int bf16, int64_t o, float (&x)[8]) {
+  if (bf16) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + o);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __builtin_bit_cast(float, v[k] << 16);
+      x[2 * k + 1] = __builtin_bit_cast(float, v[k] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 u = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + o);
+    const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + o + 4);
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+  }
+}
+
+__device__ __forceinline__ float load1(const void* base, int bf16, int64_t o) {
+  return bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[o])
+              : reinterpret_cast<const float*>(base)[o];
+}
+
+// Adds z values (already scaled) to a running (m, s, q); zmax is their maximum.
+template <int N>
+__device__ __forceinline__ void online_add(float& m, float& s, float& q, const float (&z)[N],
+                                           float zmax) {
+  if (zmax > m) {
+    if (m != -INFINITY) {
+      const float dl = (m - zmax) * kLog2e;  // < 0
+      const float f = __builtin_amdgcn_exp2f(dl);
+      q = f * fmaf(dl, s, q);
+      s = f * s;
+    }
+    m = zmax;
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const float d = (z[k] - m) * kLog2e;
+    const float e = __builtin_amdgcn_exp2f(d);
+    s += e;
+    q = fmaf(e, d, q);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_logits(LogitsArgs a) {
+  __shared__ float pm[4], ps[4], pq[4];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int status = 0;
+  if (row == 0 && a.cu_seqlens != nullptr) {
+    for (int i = tid; i <= a.num_seqs; i += 256) {
+      const int c = a.cu_seqlens[i];
+      if (i == 0 && c != 0) status |= LLP_STATUS_LAYOUT_INVALID;
+      if (i == a.num_seqs && (int64_t)c != a.T) status |= LLP_STATUS_LAYOUT_INVALID;
+      if (i < a.num_seqs && a.cu_seqlens[i + 1] < c) status |= LLP_STATUS_LAYOUT_INVALID;
+    }
+    if (status && a.status) atomicOr(a.status, status);
+    status = 0;
+  }
+  if (a.mask != nullptr && a.mask[row] == 0) {
+    if (tid == 0) {
+      a.out_t[row] = 0.f;
+      a.out_f[row] = 0;
+      a.out_l[row] = 0.f;
+      if (a.out_e) a.out_e[row] = 0.f;
+      if (a.out_p) a.out_p[row] = 0.f;
+    }
+    return;
+  }
+  const void* xr = a.bf16 ? (const void*)(reinterpret_cast<const uint16_t*>(a.logits) + row * a.ld)
+                          : (const void*)(reinterpret_cast<const float*>(a.logits) + row * a.ld);
+  const int64_t n = a.n_real, n8 = n & ~(int64_t)7;
+  float m = -INFINITY, s = 0.f, q = 0.f;
+  for (int64_t c = 8 * (int64_t)tid; c < n8; c += 8 * 256) {
+    float x[8];
+    load8(xr, a.bf16, c, x);
+    float xm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    float z[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) z[k] = x[k] * a.c1;
+    online_add<8>(m, s, q, z, xm * a.c1);  // c1 > 0: the scaled max is the max of z
+  }
+  if (n8 + tid < n) {
+    const float z[1] = {load1(xr, a.bf16, n8 + tid) * a.c1};
+    online_add<1>(m, s, q, z, z[0]);
+  }
+  // Fold lanes in a fixed order: lane i takes lane i + off for off = 32, 16, ..., 1.
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float om = __shfl_down(m, off), os = __shfl_down(s, off), oq = __shfl_down(q, off);
+    if (lane < off) fold(m, s, q, om, os, oq);
+  }
+  if (lane == 0) {
+    pm[w] = m;
+    ps[w] = s;
+    pq[w] = q;
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  float M = -INFINITY, S = 0.f, Q = 0.f;
+  for (int g = 0; g < 4; ++g) fold(M, S, Q, pm[g], ps[g], pq[g]);
+  float lse, ent;
+  if (M == -INFINITY || !(S > 0.f)) {
+    lse = -INFINITY;
+    ent = 0.f;
+  } else {
+    const float ls = logf(S);
+    lse = M + ls;
+    ent = ls - kLn2 * (Q / S);
+  }
+  const int64_t tg = a.targets[row];
+  const bool valid = tg >= 0 && tg < a.real_vocab;
+  const int64_t loc = tg - a.offset;
+  const bool hit = valid && loc >= 0 && loc < n;
+  if (!valid) status |= LLP_STATUS_TARGET_OUT_OF_RANGE;
+  if (!hit && a.world == 1) status |= LLP_STATUS_TARGET_NOT_FOUND;
+  const float t = hit ? load1(xr, a.bf16, loc) * a.c1 : 0.f;
+  a.out_t[row] = t;
+  a.out_f[row] = hit ? 1 : 0;
+  a.out_l[row] = lse;
+  if (a.out_e) a.out_e[row] = ent;
+  if (a.out_p) a.out_p[row] = hit ? t - lse : -INFINITY;
+  if (status && a.status) atomicOr(a.status, status);
+}
+
+// ------------------------------------------------------------------------------------
+// Dense keep-mask replay ([top-p replay, "Changes" table]: local logits reused with a keep
+// mask, excluded entries -inf; [top-p replay, "Validation"]: bitwise equal to the compact
+// scorer across shard offsets and empty shards). One wave per row scans the mask row in
+// ascending column order (16 bytes per lane per step, an exclusive scan of the kept counts
+// gives each kept column its rank). With at most 64 kept columns the i-th goes to lane i and
+// the row is scored by wave_set_sum exactly as the compact scorer scores its sorted ids;
+// larger sets (which the compact form cannot hold) are scored from per-lane running sums
+// kept during the scan, folded by a fixed butterfly.
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_keep(KeepArgs a) {
+  __shared__ int list[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + w;
+  if (row >= a.T) return;
+  int status = 0;
+  if (a.mask != nullptr && a.mask[row] == 0) {
+    if (lane == 0) {
+      a.out_t[row] = 0.f;
+      a.out_f[row] = 0;
+      a.out_l[row] = 0.f;
+      if (a.out_p) a.out_p[row] = 0.f;
+    }
+    return;
+  }
+  const uint8_t* kr = a.keep + row * a.kstride;
+  const void* xr = a.bf16 ? (const void*)(reinterpret_cast<const uint16_t*>(a.logits) + row * a.lstride)
+                          : (const void*)(reinterpret_cast<const float*>(a.logits) + row * a.lstride);
+  const int64_t n = a.n_real;
+  int total = 0;                      // kept columns so far (wave-uniform)
+  float lm = -INFINITY, ls = 0.f;     // this lane's running max and sum of exp (large sets)
+  for (int64_t c0 = 0; c0 < n; c0 += 1024) {
+    const int64_t cl = c0 + 16 * lane;
+    uint32_t bits = 0;
+    if (cl < n) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(kr + cl);
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if ((v[k >> 2] >> (8 * (k & 3))) & 0xFFu) bits |= 1u << k;
+      if (n - cl < 16) bits &= (1u << (n - cl)) - 1u;
+    }
+    const int cnt = __popc(bits);
+    int pre = cnt;  // inclusive scan over lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(pre, off);
+      if (lane >= off) pre += o;
+    }
+    const int tot = __shfl(pre, 63);
+    if (tot == 0) continue;
+    int idx = total + pre - cnt;
+    while (bits) {
+      const int b = __builtin_ctz(bits);
+      bits &= bits - 1;
+      const int64_t col = cl + b;
+      if (idx < 64) list[w][idx] = (int)col;
+      const float z = load1(xr, a.bf16, col) * a.c1;
+      if (z > lm) {
+        ls = lm == -INFINITY ? 0.f : ls * expf(lm - z);
+        lm = z;
+      }
+      ls += expf(z - lm);
+      ++idx;
+    }
+    total += tot;
+  }
+  __builtin_amdgcn_wave_barrier();
+  float lse = -INFINITY;
+  if (total > 0 && total <= 64) {
+    const bool live = lane < total;
+    const float z = live ? load1(xr, a.bf16, list[w][lane]) * a.c1 : -INFINITY;
+    float M;
+    const float e = wave_set_sum(z, live, M);
+    lse = M + logf(e);
+  } else if (total > 64) {
+    float M = lm, S = ls;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float om = __shfl_xor(M, off), os = __shfl_xor(S, off);
+      const float N = fmaxf(M, om);
+      // Both lanes of a pair form the same two products and add them in lane order.
+      const float mine = M == -INFINITY ? 0.f : S * expf(M - N);
+      const float other = om == -INFINITY ? 0.f : os * expf(om - N);
+      S = (lane & off) ? other + mine : mine + other;
+      M = N;
+    }
+    lse = M + logf(S);
+  }
+  const int64_t tg = a.targets[row];
+  if (tg < 0 || tg >= a.real_vocab) status |= LLP_STATUS_TARGET_OUT_OF_RANGE;
+  const int64_t loc = tg - a.offset;
+  const bool hit = tg >= 0 && tg < a.real_vocab && loc >= 0 && loc < n && kr[loc] != 0;
+  if (lane == 0) {
+    const float t = hit ? load1(xr, a.bf16, loc) * a.c1 : 0.f;
+    a.out_t[row] = t;
+    a.out_f[row] = hit ? 1 : 0;
+    a.out_l[row] = lse;
+    if (a.out_p) a.out_p[row] = hit ? t - lse : -INFINITY;
+    if (status && a.status) atomicOr(a.status, status);
+  }
+}
+
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_layout, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
@@ -910,6 +1154,16 @@ hipError_t launch_transpose(const TransposeArgs& a, int64_t rows, hipStream_t s)
 
 hipError_t launch_dbias(const DbArgs& a, hipStream_t s) {
   if (a.n_real > 0) hipLaunchKernelGGL(k_dbias, dim3(ceil_div64(a.n_real, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_logits(const LogitsArgs& a, hipStream_t s) {
+  if (a.T > 0) hipLaunchKernelGGL(k_logits, dim3((unsigned)a.T), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_keep(const KeepArgs& a, hipStream_t s) {
+  if (a.T > 0) hipLaunchKernelGGL(k_keep, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

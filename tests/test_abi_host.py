@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
 
 STRUCTS = ["llp_info", "llp_projection", "llp_vocab_partition", "llp_token_layout",
            "llp_request", "llp_partials", "llp_final_out", "llp_bwd_in", "llp_bwd_out",
-           "llp_topp_request"]
+           "llp_topp_request", "llp_logits_request", "llp_keep_mask_request"]
 
 
 def test_ctypes_mirror_matches_header(tmp_path):
@@ -288,3 +288,92 @@ def test_backward_rejects_bad_dweight_layout():
     assert call(A.llp_bwd_out(FAKE, 4096, FAKE, 4098, None)) == A.LLP_ERR_INVALID_ARGUMENT
     assert call(A.llp_bwd_out(FAKE, 4096, FAKE + 4, 4096, None)) == A.LLP_ERR_INVALID_ARGUMENT
     assert call(A.llp_bwd_out(FAKE, 4096, FAKE, 1 << 21, None)) == A.LLP_ERR_UNSUPPORTED
+
+
+def good_logits_request(T=16, V=1000, Vp=1024):
+    r = A.llp_logits_request()
+    r.logits, r.logits_dtype, r.logits_stride = FAKE, A.LLP_DTYPE_F32, Vp
+    r.vocab.offset, r.vocab.local_size, r.vocab.real_vocab, r.vocab.padded_vocab = 0, Vp, V, Vp
+    r.vocab.rank, r.vocab.world = 0, 1
+    r.layout.num_tokens = T
+    r.target_ids = FAKE
+    r.temperature = 0.7
+    return r
+
+
+def good_keep_request(T=16, V=1000, Vp=1024):
+    r = A.llp_keep_mask_request()
+    r.logits, r.logits_dtype, r.logits_stride = FAKE, A.LLP_DTYPE_F32, Vp
+    r.keep_mask, r.keep_stride = FAKE, Vp
+    r.num_tokens = T
+    r.vocab.offset, r.vocab.local_size, r.vocab.real_vocab, r.vocab.padded_vocab = 0, Vp, V, Vp
+    r.vocab.rank, r.vocab.world = 0, 1
+    r.target_ids = FAKE
+    r.temperature = 0.7
+    r.processed_logprobs = 1
+    return r
+
+
+BAD_LOGITS = [
+    ("dtype", lambda r: setattr(r, "logits_dtype", 9)),
+    ("stride < local_size", lambda r: setattr(r, "logits_stride", 1000)),
+    ("misaligned base", lambda r: setattr(r, "logits", FAKE + 8)),
+    ("f32 stride not 16-byte rows", lambda r: setattr(r, "logits_stride", 1026)),
+    ("tau zero", lambda r: setattr(r, "temperature", 0.0)),
+    ("unknown flag", lambda r: setattr(r, "flags", 4)),
+    ("targets NULL", lambda r: setattr(r, "target_ids", None)),
+    ("real > padded", lambda r: setattr(r.vocab, "real_vocab", 2000)),
+]
+
+
+@pytest.mark.parametrize("name,fn", BAD_LOGITS, ids=[b[0] for b in BAD_LOGITS])
+def test_forward_logits_rejects_malformed_request(name, fn):
+    r = good_logits_request()
+    fn(r)
+    o = A.llp_partials(FAKE, FAKE, FAKE, None, FAKE)
+    assert A.load().llp_forward_logits(C.byref(r), C.byref(o), None) == A.LLP_ERR_INVALID_ARGUMENT
+    assert A.load().llp_last_error()
+
+
+def test_forward_logits_entropy_output_must_match_flag():
+    r = good_logits_request()
+    o = A.llp_partials(FAKE, FAKE, FAKE, FAKE, FAKE)            # entropy given, not wanted
+    assert A.load().llp_forward_logits(C.byref(r), C.byref(o), None) == A.LLP_ERR_INVALID_ARGUMENT
+    r.flags = A.LLP_FLAG_WANT_ENTROPY
+    o = A.llp_partials(FAKE, FAKE, FAKE, None, FAKE)            # wanted, not given
+    assert A.load().llp_forward_logits(C.byref(r), C.byref(o), None) == A.LLP_ERR_INVALID_ARGUMENT
+
+
+def test_new_entry_points_valid_requests_pass_validation():
+    """Well-formed requests get past validation; without a device they fail afterwards."""
+    o = A.llp_partials(FAKE, FAKE, FAKE, None, FAKE)
+    for st in (A.load().llp_forward_logits(C.byref(good_logits_request()), C.byref(o), None),
+               A.load().llp_keep_mask_replay(C.byref(good_keep_request()), C.byref(o), None)):
+        assert st not in (A.LLP_OK, A.LLP_ERR_INVALID_ARGUMENT) or \
+            "llp_open" in A.load().llp_last_error().decode()
+
+
+BAD_KEEP = [
+    ("raw logprobs", lambda r: setattr(r, "processed_logprobs", 0)),
+    ("keep stride < local_size", lambda r: setattr(r, "keep_stride", 1000)),
+    ("keep stride not 16", lambda r: setattr(r, "keep_stride", 1032 + 4)),
+    ("keep misaligned", lambda r: setattr(r, "keep_mask", FAKE + 4)),
+    ("logits misaligned", lambda r: setattr(r, "logits", FAKE + 2)),
+    ("dtype", lambda r: setattr(r, "logits_dtype", 0)),
+    ("tau nan", lambda r: setattr(r, "temperature", float("nan"))),
+    ("keep NULL", lambda r: setattr(r, "keep_mask", None)),
+]
+
+
+@pytest.mark.parametrize("name,fn", BAD_KEEP, ids=[b[0] for b in BAD_KEEP])
+def test_keep_mask_replay_rejects_malformed_request(name, fn):
+    r = good_keep_request()
+    fn(r)
+    o = A.llp_partials(FAKE, FAKE, FAKE, None, FAKE)
+    assert A.load().llp_keep_mask_replay(C.byref(r), C.byref(o), None) == A.LLP_ERR_INVALID_ARGUMENT
+
+
+def test_keep_mask_replay_rejects_entropy_output():
+    r = good_keep_request()
+    o = A.llp_partials(FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert A.load().llp_keep_mask_replay(C.byref(r), C.byref(o), None) == A.LLP_ERR_INVALID_ARGUMENT
