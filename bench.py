@@ -126,6 +126,71 @@ def cpu_baseline(rows: int = 2560) -> dict:
                       f"(H=4096, V=151669/151936), {dt:.1f} s on {threads} BLAS threads"}
 
 
+def measure_next_rows(llp, logits, rids, rtg, shards, stream, reps=10):
+    """The rows beyond the step, on the same config-5 logits [4096, 151936] fp32, timed with
+    HIP events on the launch stream (mean over `reps` calls after a warm-up call):
+    the logits-input forward over the full real vocabulary (HBM bound: it reads every real
+    logit once), and the dense keep-mask replay of the same nuclei over the 4 shards next to
+    the compact replay (the dense pass reads the whole T x V_loc mask)."""
+    import torch
+
+    def timed(fn):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps  # ms
+
+    log("logits-input forward and dense keep mask (config-5 logits)")
+    lf_ms = timed(lambda: llp.forward_logits(logits, rtg, temperature=TAU, real_vocab=VR,
+                                             padded_vocab=VP))
+    lf_bytes = T * VR * 4 + T * (8 + 17)      # every real logit once; target in, partials out
+    keep = torch.zeros((T, VP), dtype=torch.uint8, device="cuda")
+    valid = rids >= 0
+    keep[torch.arange(T, device="cuda")[:, None].expand_as(rids)[valid], rids[valid]] = 1
+
+    # The replay calls take microseconds at T=4096, less than a call's host overhead, so the
+    # dense/compact comparison runs on config 5 tiled 16x (T=65536, the size the cost ratio
+    # is quoted at): the same rows repeated.
+    rep = 16
+    logits_b, keep_b = logits.repeat(rep, 1), keep.repeat(rep, 1)
+    rids_b, rtg_b = rids.repeat(rep, 1), rtg.repeat(rep)
+    del keep
+    Tb = T * rep
+
+    def dense():
+        for r, (off, n) in enumerate(shards):
+            llp.keep_mask_replay(logits_b[:, off:off + n], keep_b[:, off:off + n], rtg_b,
+                                 temperature=TAU, offset=off, real_vocab=VR, padded_vocab=VP,
+                                 rank=r, world=4, local_size=n)
+
+    def compact():
+        for r, (off, n) in enumerate(shards):
+            llp.top_p_replay(logits_b[:, off:off + n], rids_b, rtg_b, temperature=TAU,
+                             offset=off, real_vocab=VR, padded_vocab=VP, rank=r, world=4,
+                             local_size=n)
+
+    dense_ms, compact_ms = timed(dense), timed(compact)
+    dense_bytes = Tb * VR * 1 + rep * int(valid.sum().item()) * 4 + Tb * 4 * (8 + 13)
+    del logits_b, keep_b, rids_b, rtg_b
+    return {
+        "logits_forward": {"us": lf_ms * 1e3, "algorithmic_bytes": lf_bytes,
+                           "GBps": lf_bytes / (lf_ms * 1e-3) / 1e9, "peak_GBps": PEAK_HBM_GBS,
+                           "frac": lf_bytes / (lf_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                           "workload": "fp32 logits [4096, 151936], 151669 real columns, "
+                                       "entropy on"},
+        "keep_mask_replay": {"dense_us": dense_ms * 1e3, "compact_us": compact_ms * 1e3,
+                             "dense_over_compact": dense_ms / compact_ms,
+                             "dense_algorithmic_bytes": dense_bytes,
+                             "dense_GBps": dense_bytes / (dense_ms * 1e-3) / 1e9,
+                             "workload": "config-5 nuclei tiled 16x (T=65536) over 4 shards "
+                                         "of 37984 columns"},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,6 +322,7 @@ def main():
         "top_p": {"us": topp_ms * 1e3, "algorithmic_bytes": topp_bytes,
                   "GBps": topp_bytes / (topp_ms * 1e-3) / 1e9, "peak_GBps": PEAK_HBM_GBS},
     }
+    res.update(measure_next_rows(llp, logits, rids, rtg, shards, stream))
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_rows} rows")
         del W, h, logits, dW, dH

@@ -1021,40 +1021,52 @@ __global__ __launch_bounds__(256) void k_keep(KeepArgs a) {
   const int64_t n = a.n_real;
   int total = 0;                      // kept columns so far (wave-uniform)
   float lm = -INFINITY, ls = 0.f;     // this lane's running max and sum of exp (large sets)
-  for (int64_t c0 = 0; c0 < n; c0 += 1024) {
-    const int64_t cl = c0 + 16 * lane;
-    uint32_t bits = 0;
-    if (cl < n) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(kr + cl);
+  for (int64_t c4 = 0; c4 < n; c4 += 4096) {
+    // Four 1 KiB pieces per pass, loaded together (independent loads in flight), then
+    // scanned in column order.
+    u32x4 v4[4];
 #pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if ((v[k >> 2] >> (8 * (k & 3))) & 0xFFu) bits |= 1u << k;
-      if (n - cl < 16) bits &= (1u << (n - cl)) - 1u;
+    for (int p = 0; p < 4; ++p) {
+      const int64_t cl = c4 + 1024 * p + 16 * lane;
+      v4[p] = cl < n ? *reinterpret_cast<const u32x4*>(kr + cl) : u32x4{0u, 0u, 0u, 0u};
     }
-    const int cnt = __popc(bits);
-    int pre = cnt;  // inclusive scan over lanes
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(pre, off);
-      if (lane >= off) pre += o;
-    }
-    const int tot = __shfl(pre, 63);
-    if (tot == 0) continue;
-    int idx = total + pre - cnt;
-    while (bits) {
-      const int b = __builtin_ctz(bits);
-      bits &= bits - 1;
-      const int64_t col = cl + b;
-      if (idx < 64) list[w][idx] = (int)col;
-      const float z = load1(xr, a.bf16, col) * a.c1;
-      if (z > lm) {
-        ls = lm == -INFINITY ? 0.f : ls * expf(lm - z);
-        lm = z;
+    for (int p = 0; p < 4; ++p) {
+      const int64_t cl = c4 + 1024 * p + 16 * lane;
+      if (c4 + 1024 * p >= n) break;
+      uint32_t bits = 0;
+      if (cl < n) {
+        const u32x4 v = v4[p];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if ((v[k >> 2] >> (8 * (k & 3))) & 0xFFu) bits |= 1u << k;
+        if (n - cl < 16) bits &= (1u << (n - cl)) - 1u;
       }
-      ls += expf(z - lm);
-      ++idx;
+      const int cnt = __popc(bits);
+      int pre = cnt;  // inclusive scan over lanes
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(pre, off);
+        if (lane >= off) pre += o;
+      }
+      const int tot = __shfl(pre, 63);
+      if (tot == 0) continue;
+      int idx = total + pre - cnt;
+      while (bits) {
+        const int b = __builtin_ctz(bits);
+        bits &= bits - 1;
+        const int64_t col = cl + b;
+        if (idx < 64) list[w][idx] = (int)col;
+        const float z = load1(xr, a.bf16, col) * a.c1;
+        if (z > lm) {
+          ls = lm == -INFINITY ? 0.f : ls * expf(lm - z);
+          lm = z;
+        }
+        ls += expf(z - lm);
+        ++idx;
+      }
+      total += tot;
     }
-    total += tot;
   }
   __builtin_amdgcn_wave_barrier();
   float lse = -INFINITY;
