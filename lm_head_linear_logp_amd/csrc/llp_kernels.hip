@@ -577,7 +577,7 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArg
       const int tn = wn * 128 + ni * 32 + (lane & 31);
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        uint32_t pk[2];
+        float gv[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = rg * 4 + u;
@@ -589,12 +589,9 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArg
           if constexpr (ENT) g -= de[ni] * p * (x * a.c1 - ez[ni]);
           g *= a.c1;
           if (!live[ni] || (TAIL && vbase + vl >= a.n_real)) g = 0.f;
-          const uint32_t hb = f32_to_bf16_rne(g);
-          if (u & 1)
-            pk[u >> 1] |= hb << 16;
-          else
-            pk[u >> 1] = hb;
+          gv[u] = g;
         }
+        const uint32_t pk[2] = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
         const int vl0 = wm * 128 + mi * 32 + mfma_row(rg * 4, lane);
         *reinterpret_cast<uint2*>(smem + tn * GT_STRIDE + vl0) = make_uint2(pk[0], pk[1]);
       }
@@ -696,7 +693,7 @@ __global__ __launch_bounds__(256) void k_dh_reduce(DhReduceArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      pk[u] = (uint32_t)f32_to_bf16_rne(s[2 * u]) | ((uint32_t)f32_to_bf16_rne(s[2 * u + 1]) << 16);
+      pk[u] = pack_bf16x2(s[2 * u], s[2 * u + 1]);
   }
   *reinterpret_cast<u32x4*>(a.dH + t * a.ldd + n) = u32x4{pk[0], pk[1], pk[2], pk[3]};
 }

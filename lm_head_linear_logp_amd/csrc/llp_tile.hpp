@@ -56,10 +56,12 @@ __device__ __forceinline__ void vocab_token_tile(int tile, int nvt, int ntb, int
   tb = gi / gsz;
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two floats to packed bf16 (first in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
