@@ -549,9 +549,10 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArg
   const int wm = wave & 1, wn = wave >> 1;
   const int vbase = v0 + wm * 128;
   const float c1l = a.c1 * kLog2e;
-  float lsel[4], dl[4], de[4], ez[4];
+  // Per row: dlc = dlogp / tau and dec = dentropy / tau, both 0 for rows past the count and rows
+  // no gradient flows into, so those rows come out as exact (+0) zeros in G.
+  float lsel[4], dlc[4], dec[4], ez[4];
   int tl[4];
-  bool live[4];
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
     const int j = j0 + wn * 128 + ni * 32 + (lane & 31);
@@ -559,12 +560,13 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArg
     const int row = a.scored[jj];
     const float lse = a.lse[row];
     lsel[ni] = lse * kLog2e;
-    dl[ni] = a.dlogp[row];
-    de[ni] = ENT ? a.dent[row] : 0.f;
+    const float dl = a.dlogp[row];
+    const float de = ENT ? a.dent[row] : 0.f;
+    const bool live = j < Ts && (dl != 0.f || de != 0.f);
+    dlc[ni] = live ? dl * a.c1 : 0.f;
+    dec[ni] = live ? de * a.c1 : 0.f;
     ez[ni] = ENT ? lse - a.ent[row] : 0.f;
     tl[ni] = a.tloc[jj] - vbase;
-    // Rows past the count, and rows no gradient flows into, are exact zeros in G.
-    live[ni] = j < Ts && (dl[ni] != 0.f || de[ni] != 0.f);
   }
   // Stage the bf16 tile as Gs[token][vocab] in LDS, then write full rows.
   __syncthreads();
@@ -583,12 +585,12 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArg
           const int r = rg * 4 + u;
           const int vl = mi * 32 + mfma_row(r, lane);
           const float x = xval<BMODE>(acc_read(acc[mi][ni][r]), b, r);
-          // p = exp(z - lse) = 2^(x c1 log2(e) - lse log2(e)).
+          // p = exp(z - lse) = 2^(x c1 log2(e) - lse log2(e));
+          // g = (dlogp (1[v = t] - p) - dentropy p (z - E z)) / tau.
           const float p = __builtin_amdgcn_exp2f(fmaf(x, c1l, -lsel[ni]));
-          float g = dl[ni] * ((vl == tl[ni] ? 1.f : 0.f) - p);
-          if constexpr (ENT) g -= de[ni] * p * (x * a.c1 - ez[ni]);
-          g *= a.c1;
-          if (!live[ni] || (TAIL && vbase + vl >= a.n_real)) g = 0.f;
+          float g = fmaf(-dlc[ni], p, vl == tl[ni] ? dlc[ni] : 0.f);
+          if constexpr (ENT) g = fmaf(-dec[ni] * p, fmaf(x, a.c1, -ez[ni]), g);
+          if (TAIL && vbase + vl >= a.n_real) g = 0.f;
           gv[u] = g;
         }
         const uint32_t pk[2] = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
