@@ -376,3 +376,76 @@ def test_backward_accumulates_dweight(llp):
     one = run_backward(llp, case, f["lse"], dlogp)
     two = run_backward(llp, case, f["lse"], dlogp, dweight=one["dweight"].clone())
     np.testing.assert_allclose(host(two["dweight"]), 2 * host(one["dweight"]), rtol=1e-6, atol=1e-9)
+
+
+def test_backward_vocab_shards_sum_to_unsharded(llp):
+    """Per-shard backward with the merged lse: each shard matches the oracle's shard backward,
+    dhidden summed over the shards and dweight assembled from them match the unsharded
+    gradients. Cuts include an empty shard, one that ends at the last real column and one that
+    holds padding only (zero dhidden, dweight rows untouched)."""
+    T, H, Vr, Vp, tau = 300, 256, 900, 1024, 0.7
+    case = synth.small_case(T, H, Vr, Vp, tau, case_id=72, mask_frac=0.2, w_std=0.1)
+    f = oracle.forward(case["hidden"], case["weight"], None, tau, case["targets"], case["mask"],
+                       Vr)
+    g = synth.rng(72, 3)
+    dlogp = g.standard_normal(T) * case["mask"]
+    dent = g.standard_normal(T) * case["mask"]
+    full = oracle.backward(case["hidden"], case["weight"], None, tau, case["targets"],
+                           case["mask"], 0, Vp, Vr, f["lse"], dlogp, dent, f["entropy"])
+    cuts = [0, 256, 520, 520, 900, 1024]
+    dW = torch.zeros((Vp, H), dtype=torch.float32, device="cuda")
+    dH_sum = np.zeros((T, H))
+    for r, (lo, hi) in enumerate(zip(cuts[:-1], cuts[1:])):
+        say(f"backward shard {r} [{lo}, {hi})")
+        out = run_backward(llp, dict(case, weight=case["weight"][lo:hi]), f["lse"], dlogp, dent,
+                           f["entropy"], offset=lo, rank=r, world=len(cuts) - 1,
+                           dweight=dW[lo:hi])
+        dH = oracle.bf16_to_f64(host(out["dhidden"]))
+        ref = oracle.backward(case["hidden"], case["weight"][lo:hi], None, tau, case["targets"],
+                              case["mask"], lo, hi - lo, Vr, f["lse"], dlogp, dent,
+                              f["entropy"])
+        if lo >= Vr or hi == lo:
+            assert np.all(dH == 0)
+        else:
+            r1 = normwise_rel(dH, ref["dhidden"])
+            say(f"  rel dH {r1:.2e}")
+            assert r1 <= GRAD_RTOL
+        dH_sum += dH
+    r1 = normwise_rel(dH_sum, full["dhidden"])
+    r2 = normwise_rel(host(dW), full["dweight"])
+    say(f"summed shards: rel dH {r1:.2e} dW {r2:.2e}")
+    assert r1 <= GRAD_RTOL and r2 <= GRAD_RTOL
+    assert np.all(host(dW)[Vr:] == 0)
+
+
+def test_backward_f32_bias_masked_and_empty(llp):
+    """fp32 bias: dH, dW, db against the oracle. All rows masked: dhidden zero, dweight and
+    dbias unchanged. No rows at all: nothing written."""
+    T, H, Vr, Vp, tau = 200, 128, 500, 512, 0.9
+    case = synth.small_case(T, H, Vr, Vp, tau, case_id=73, mask_frac=0.3, with_bias=True,
+                            w_std=0.1)
+    f = oracle.forward(case["hidden"], case["weight"], case["bias"], tau, case["targets"],
+                       case["mask"], Vr)
+    dlogp = synth.rng(73, 3).standard_normal(T) * case["mask"]
+    ref = oracle.backward(case["hidden"], case["weight"], case["bias"], tau, case["targets"],
+                          case["mask"], 0, Vp, Vr, f["lse"], dlogp)
+    out = run_backward(llp, case, f["lse"], dlogp, bias_dtype=torch.float32)
+    r1 = normwise_rel(oracle.bf16_to_f64(host(out["dhidden"])), ref["dhidden"])
+    r2 = normwise_rel(host(out["dweight"]), ref["dweight"])
+    r3 = normwise_rel(host(out["dbias"]), ref["dbias"])
+    say(f"f32 bias: rel dH {r1:.2e} dW {r2:.2e} db {r3:.2e}")
+    assert r1 <= GRAD_RTOL and r2 <= GRAD_RTOL and r3 <= GRAD_RTOL
+
+    ones_w = torch.ones((Vp, H), dtype=torch.float32, device="cuda")
+    ones_b = torch.ones(Vp, dtype=torch.float32, device="cuda")
+    masked = run_backward(llp, dict(case, mask=np.zeros(T, np.uint8)), f["lse"], dlogp,
+                          bias_dtype=torch.float32, dweight=ones_w, dbias=ones_b)
+    assert np.all(host(masked["dhidden"]) == 0)
+    assert np.all(host(ones_w) == 1) and np.all(host(ones_b) == 1)
+
+    empty = dict(case, T=0, hidden=case["hidden"][:0], targets=case["targets"][:0],
+                 mask=case["mask"][:0])
+    out0 = run_backward(llp, empty, f["lse"][:0], dlogp[:0], bias_dtype=torch.float32,
+                        dweight=ones_w, dbias=ones_b)
+    assert out0["dhidden"].numel() == 0
+    assert np.all(host(ones_w) == 1) and np.all(host(ones_b) == 1)
