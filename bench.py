@@ -126,6 +126,30 @@ def cpu_baseline(rows: int = 2560) -> dict:
                       f"(H=4096, V=151669/151936), {dt:.1f} s on {threads} BLAS threads"}
 
 
+def measure_vendor_gemm(h, W, stream, reps=10):
+    """Context for the forward's roofline fraction: the vendor library's plain GEMM of the same
+    operands (torch.matmul -> hipBLASLt), h [4096, 4096] x W^T over the padded vocabulary, bf16
+    logits out and no epilogue. It is not part of the path; it shows the MFMA rate a tuned
+    library reaches on this shape under the chip's power limit. HIP events on the stream."""
+    import torch
+    out = torch.empty((h.shape[0], W.shape[0]), dtype=torch.bfloat16, device=h.device)
+    wt = W.t()
+    torch.matmul(h, wt, out=out)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        torch.matmul(h, wt, out=out)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del out
+    flop = 2.0 * h.shape[0] * h.shape[1] * W.shape[0]
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"vendor_gemm": {"what": "torch.matmul (hipBLASLt) of h [4096, 4096] by W^T "
+                                    "[4096, 151936], bf16 out, no epilogue",
+                            "us": ms * 1e3, "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS}}
+
+
 def measure_next_rows(llp, logits, rids, rtg, shards, stream, reps=10):
     """The rows beyond the step, on the same config-5 logits [4096, 151936] fp32, timed with
     HIP events on the launch stream (mean over `reps` calls after a warm-up call):
@@ -323,6 +347,7 @@ def main():
                   "GBps": topp_bytes / (topp_ms * 1e-3) / 1e9, "peak_GBps": PEAK_HBM_GBS},
     }
     res.update(measure_next_rows(llp, logits, rids, rtg, shards, stream))
+    res.update(measure_vendor_gemm(h, W, stream))
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_rows} rows")
         del W, h, logits, dW, dH
