@@ -700,80 +700,68 @@ __global__ __launch_bounds__(256) void k_dh_reduce(DhReduceArgs a) {
   *reinterpret_cast<u32x4*>(a.dH + t * a.ldd + n) = u32x4{pk[0], pk[1], pk[2], pk[3]};
 }
 
-// dweight[m0 .. m0+255, n0 .. n0+255] += acc, through LDS (the pipeline's stages are free
-// here). Four phases, one per 32-row block mi of every wave: phase p covers tile rows
-// wm*128 + 32p + (0..31) for wm = 0, 1, i.e. 64 rows of 1 KiB. Its old values arrive by direct
-// global->LDS loads (no registers, a whole phase in flight; phases p+1, p+2 stream in while p
-// is summed, two 64 KiB buffers); each lane adds its accumulators in place, then every wave
-// writes 16 whole rows back with 16-byte stores. Rows at or past n_real and columns at or past
-// H are neither read into a result nor written (their loads read a clamped in-bounds address).
-constexpr int DWB_ROWS = 64;                 // rows per phase
-constexpr int DWB_BYTES = DWB_ROWS * BN * 4;  // 64 KiB per phase buffer
-static_assert(2 * DWB_BYTES <= dma::LDS_BYTES, "dweight staging fits the pipeline LDS");
+// dweight += the tile, straight from registers. The tile is computed transposed (M = hidden
+// columns n, N = vocabulary rows m), so the 4 accumulators r = 4q .. 4q+3 of block (mi, ni) are
+// 4 consecutive hidden columns of one dweight row: lane l holds row
+// m0 + wn*128 + ni*32 + (l & 31), columns n0 + wm*128 + mi*32 + 8q + 4(l >> 5) + 0..3, one
+// 16-byte chunk, which it loads, adds to (old + sum, in fp32) and stores back. Chunks of rows
+// at or past n_real or columns at or past H are masked: they are neither read into a result
+// nor written. The compiler places every wait (loads and stores share one counter).
+constexpr uint32_t DW_MASKED = 0xFFFFFFFFu;
+struct DwTile {
+  uint32_t off[4][4][4];  // [mi][ni][q] byte offset from the tile's first element, or masked
+};
 
-__device__ __forceinline__ void dw_phase_load(const DwArgs& a, int m0, int n0, int nv, int nc, int p,
-                                              unsigned char* buf) {
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.dW + (int64_t)m0 * a.lddw + n0), (short)0,
-      (int)(uint32_t)(((int64_t)(nv - 1) * a.lddw + nc) * 4), 0x00020000);
-  const uint32_t voff = 4 * lane < nc ? 16u * lane : 0u;
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int q = 16 * w + u;                          // phase row (uniform)
-    int lr = (q >> 5) * 128 + 32 * p + (q & 31);       // tile row
-    lr = lr < nv ? lr : nv - 1;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(buf + q * (BN * 4)), 16, voff,
-        (int)((int64_t)lr * a.lddw * 4), 0, 0);
-  }
-}
-
-__device__ __forceinline__ void dw_accumulate(const f32x16 (&acc)[4][4], const DwArgs& a, int m0,
-                                              int n0, uint16_t* smem) {
+__device__ __forceinline__ void dw_tile_setup(const DwArgs& a, int m0, int n0, DwTile& t) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int nv = a.n_real - m0 < BM ? (int)(a.n_real - m0) : BM;
   const int nc = a.H - n0 < BN ? a.H - n0 : BN;
-  unsigned char* lds = reinterpret_cast<unsigned char*>(smem);
-  // VMEM order per wave: L0 L1 | S0 L2 | S1 L3 | S2 | S3, 16 loads per L and at most 16 stores
-  // per S (a wave skips the stores of rows past n_real). Completion is in order, so phase p's
-  // loads (and the stores before them) have landed once at most 16 instructions are pending
-  // for p < 3 (exactly the 16 loads of phase p+1 or p+2 were issued after them) and 0 for p = 3.
-  dw_phase_load(a, m0, n0, nv, nc, 0, lds);
-  dw_phase_load(a, m0, n0, nv, nc, 1, lds + DWB_BYTES);
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    unsigned char* buf = lds + (p & 1) * DWB_BYTES;
-    if (p < 3) dma::wait_vmem_le<16>();
-    else dma::wait_vmem_le<0>();
-    dma::lds_barrier();
-    // In place: buf[row][col] += acc for this lane's 64 elements of block mi = p.
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = wm * 32 + mfma_row(r, lane);
-        const int c = wn * 128 + ni * 32 + (lane & 31);
-        float* e = reinterpret_cast<float*>(buf + q * (BN * 4) + c * 4);
-        *e += acc_read(acc[p][ni][r]);
+      for (int q = 0; q < 4; ++q) {
+        const int m = wn * 128 + ni * 32 + (lane & 31);
+        const int n = wm * 128 + mi * 32 + 8 * q + 4 * (lane >> 5);
+        t.off[mi][ni][q] = (m < nv && n < nc) ? (uint32_t)(((int64_t)m * a.lddw + n) * 4)
+                                              : DW_MASKED;
       }
-    dma::lds_barrier();
-    // Wave w writes phase rows 16w .. 16w+15, 16 bytes per lane.
+}
+
+// Old values of block row mi (16 chunks per lane): plain 16-byte loads, a masked chunk reading
+// the tile's first one instead (its value is never stored).
+__device__ __forceinline__ void dw_load(const DwTile& t, const float* base, int mi,
+                                        u32x4 (&v)[16]) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int q = 16 * wave + u;
-      const int lr = (q >> 5) * 128 + 32 * p + (q & 31);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(buf + q * (BN * 4) + 16 * lane);
-      if (lr < nv && 4 * lane < nc)
-        *reinterpret_cast<u32x4*>(a.dW + (int64_t)(m0 + lr) * a.lddw + n0 + 4 * lane) = v;
+  for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t o = t.off[mi][ni][q];
+      v[4 * ni + q] = *reinterpret_cast<const u32x4*>(
+          reinterpret_cast<const unsigned char*>(base) + (o == DW_MASKED ? 0u : o));
     }
-    if (p + 2 < 4) {
-      dma::lds_barrier();  // every wave has read this buffer
-      dw_phase_load(a, m0, n0, nv, nc, p + 2, buf);
+}
+
+__device__ __forceinline__ void dw_add_store(const f32x16 (&acc)[4][4], const DwTile& t,
+                                             float* base, int mi, const u32x4 (&v)[16]) {
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // Through a scalar: a bit cast applied to a vector element in place is miscompiled
+        // (the load is narrowed to its first element).
+        const uint32_t old = v[4 * ni + q][e];
+        o[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, old) +
+                                                acc_read(acc[mi][ni][4 * q + e]));
+      }
+      const uint32_t off = t.off[mi][ni][q];
+      if (off != DW_MASKED)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(base) + off) = o;
     }
-  }
-  dma::wait_vmem_le<0>();
 }
 
 // dweight[v, n] += sum_j G[j, v] hgT[n, j] over the scored rows j in ascending order
@@ -785,25 +773,37 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int Ts = *a.count;
   if (Ts <= 0) return;
   const int m0 = mt * BM, n0 = nt * BN;
-  // A: G itself, K-major: rows = scored rows (zero from the count to the next whole step),
-  // columns m0 .. m0+255 (inside the padded vocabulary capacity). B: hgT rows n0 .. (< H).
-  // K = scored rows rounded up to whole steps.
+  // A (tile rows): hgT rows n0 .. (< H), K = scored rows rounded up to whole steps.
+  // B (tile columns): G itself, K-major: rows = scored rows (zero from the count to the next
+  // whole step), columns m0 .. m0+255 (inside the padded vocabulary capacity).
   const int nn = a.H - n0 < BN ? a.H - n0 : BN;
   const int nk = (Ts + dma::BKD - 1) / dma::BKD;
   const int64_t kb = (int64_t)nk * dma::BKD;
-  dma::LoaderK la;
-  la.init(a.G + m0, a.ldg, (int)kb - 1, BM);
-  dma::Loader lb;
-  lb.init(a.hgT + (int64_t)n0 * a.ldk, (uint64_t)((nn - 1) * a.ldk + kb) * 2);
+  dma::Loader la;
+  la.init(a.hgT + (int64_t)n0 * a.ldk, (uint64_t)((nn - 1) * a.ldk + kb) * 2);
 #pragma unroll
   for (int u = 0; u < dma::NI; ++u) {
     const int r = dma::Loader::row_of(u);
-    lb.set(u, r < nn ? r : nn - 1, a.ldk);
+    la.set(u, r < nn ? r : nn - 1, a.ldk);
   }
+  dma::LoaderK lb;
+  lb.init(a.G + m0, a.ldg, (int)kb - 1, BM);
+  DwTile t;
+  dw_tile_setup(a, m0, n0, t);
+  float* dwt = a.dW + (int64_t)m0 * a.lddw + n0;
   f32x16 acc[4][4];
   zero_acc(acc);
-  dma::mainloop(la, lb, 0, (Ts + dma::BKD - 1) / dma::BKD, smem, acc);
-  dw_accumulate(acc, a, m0, n0, smem);
+  dma::mainloop(la, lb, 0, nk, smem, acc);
+  // Two block rows of old values in flight at a time.
+  u32x4 v0[16], v1[16];
+  dw_load(t, dwt, 0, v0);
+  dw_load(t, dwt, 1, v1);
+  dw_add_store(acc, t, dwt, 0, v0);
+  dw_load(t, dwt, 2, v0);
+  dw_add_store(acc, t, dwt, 1, v1);
+  dw_load(t, dwt, 3, v1);
+  dw_add_store(acc, t, dwt, 2, v0);
+  dw_add_store(acc, t, dwt, 3, v1);
 }
 
 // out[c][r] = in[row(r)][c] for r < nvalid (zero for nvalid <= r < the grid's rows), 64 x 64
