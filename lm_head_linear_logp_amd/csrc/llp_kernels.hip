@@ -87,24 +87,23 @@ __global__ __launch_bounds__(1024) void k_layout(LayoutArgs a) {
 // MFMA operand A = weight rows (vocabulary, M), B = hidden rows (tokens, N): each lane owns
 // one token column, so the per-row reductions run down its own registers first.
 // ------------------------------------------------------------------------------------
-// Bias modes of the fused tiles: none, bf16 or fp32 vector (one instantiation each).
-constexpr int BIAS_NONE = 0, BIAS_BF16 = 1, BIAS_F32 = 2;
-
+// The bias enters as the accumulators' starting value: z * tau = bias + h.W^T comes straight
+// out of the MFMAs, so neither epilogue reads the bias, and every bias mode runs the no-bias
+// epilogue with its register footprint. The forward and the gradient tile start the same way,
+// so both see the same z.
+//
 // Bias of this lane's 16 accumulator rows of the 32-row block at vb: rows
 // vb + 8g + 4(lane/32) + 0..3 for g = 0..3 (mfma_row), i.e. four runs of four consecutive
 // rows, each read with one vector load (the bias is 16-byte aligned for fp32, 8-byte for
 // bf16). Rows at or past n_real (only in the shard's last tile) read as 0.
-template <int BMODE, bool TAIL>
+template <bool F32>
 __device__ __forceinline__ void bias16(const void* bias, int vb, int lane, int64_t n_real,
                                        float (&b)[16]) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int v = vb + 8 * g + 4 * (lane >> 5);
-    if constexpr (BMODE == BIAS_NONE) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) b[4 * g + u] = 0.f;
-    } else if (!TAIL || v + 3 < n_real) {
-      if constexpr (BMODE == BIAS_F32) {
+    if (v + 3 < n_real) {
+      if constexpr (F32) {
         const float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(bias) + v);
         b[4 * g] = x.x;
         b[4 * g + 1] = x.y;
@@ -122,30 +121,42 @@ __device__ __forceinline__ void bias16(const void* bias, int vb, int lane, int64
       for (int u = 0; u < 4; ++u) {
         float x = 0.f;
         if (v + u < n_real)
-          x = BMODE == BIAS_F32 ? reinterpret_cast<const float*>(bias)[v + u]
-                                : bf16_to_f32(reinterpret_cast<const uint16_t*>(bias)[v + u]);
+          x = F32 ? reinterpret_cast<const float*>(bias)[v + u]
+                  : bf16_to_f32(reinterpret_cast<const uint16_t*>(bias)[v + u]);
         b[4 * g + u] = x;
       }
     }
   }
 }
 
-// One bias value (the target column's), 0 without a bias.
-template <int BMODE>
-__device__ __forceinline__ float bias1(const void* bias, int v) {
-  if constexpr (BMODE == BIAS_F32) return reinterpret_cast<const float*>(bias)[v];
-  if constexpr (BMODE == BIAS_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(bias)[v]);
-  return 0.f;
+// Starting accumulators of a vocabulary x token tile at v0: each lane's rows get their bias (the
+// same for all its token blocks).
+template <bool F32>
+__device__ __forceinline__ void bias_acc(f32x16 (&acc)[4][4], const void* bias, int v0,
+                                         int64_t n_real) {
+  const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) & 1;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    float b[16];
+    bias16<F32>(bias, v0 + wm * 128 + mi * 32, lane, n_real, b);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = b[r];
+  }
 }
 
-// x = acc (+ bias) of accumulator element r; z = x * c1.
-template <int BMODE>
-__device__ __forceinline__ float xval(float acc, const float (&b)[16], int r) {
-  if constexpr (BMODE == BIAS_NONE) return acc;
-  return acc + b[r];
+// The same, or 0 without a bias (mode chosen at run time).
+__device__ __forceinline__ void init_acc(f32x16 (&acc)[4][4], const void* bias, bool bias_f32,
+                                         int v0, int64_t n_real) {
+  if (bias == nullptr) zero_acc(acc);
+  else if (bias_f32) bias_acc<true>(acc, bias, v0, n_real);
+  else bias_acc<false>(acc, bias, v0, n_real);
 }
 
-template <bool TAIL, int BMODE>
+constexpr int BIAS_NONE = 0, BIAS_BF16 = 1, BIAS_F32 = 2;
+
+template <bool TAIL>
 __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const FwdArgs& a, int vt,
                                              int v0, int j0, int Ts, uint16_t* smem) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -160,13 +171,11 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const Fw
   for (int ni = 0; ni < 4; ++ni) mx[ni] = -INFINITY;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
-    float b[16];
-    bias16<BMODE, TAIL>(a.bias, vbase + mi * 32, lane, a.n_real, b);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = xval<BMODE>(acc[mi][ni][r], b, r);
+        float x = acc[mi][ni][r];
         if (TAIL && vbase + mi * 32 + mfma_row(r, lane) >= a.n_real) x = -INFINITY;
         mx[ni] = fmaxf(mx[ni], x);
       }
@@ -189,13 +198,11 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const Fw
   float sv[4] = {0.f, 0.f, 0.f, 0.f}, qv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
-    float b[16];
-    bias16<BMODE, TAIL>(a.bias, vbase + mi * 32, lane, a.n_real, b);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float d2 = fmaf(xval<BMODE>(acc[mi][ni][r], b, r), c1l, -ml[ni]);
+        float d2 = fmaf(acc[mi][ni][r], c1l, -ml[ni]);
         // Excluded column: 2^-1e30 = 0 and 0 * -1e30 = 0.
         if (TAIL && vbase + mi * 32 + mfma_row(r, lane) >= a.n_real) d2 = -1e30f;
         const float e = __builtin_amdgcn_exp2f(d2);
@@ -237,10 +244,7 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const Fw
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (mi == mt && r == rt) t = acc[mi][ni][r];
-      if (mine) {
-        if constexpr (BMODE != BIAS_NONE) t += bias1<BMODE>(a.bias, vbase + tl);
-        a.tz[j] = t * a.c1;
-      }
+      if (mine) a.tz[j] = t * a.c1;
     }
   }
 }
@@ -270,8 +274,8 @@ __device__ __forceinline__ void weight_hidden_loaders(const uint16_t* W, int64_t
 static_assert(6 * 256 * 4 <= dma::LDS_BYTES, "forward epilogue LDS");
 static_assert(dma::BKD == KSTEP, "K step shared with the host");
 
-// One kernel per bias mode: each gets its own register allocation (the bias variants need
-// more registers in the epilogue than the common no-bias case).
+// One kernel per bias mode, differing only in how the accumulators start: a run-time choice
+// there makes the compiler spill accumulators in the epilogue.
 template <int BMODE>
 __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
@@ -283,12 +287,13 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   dma::Loader la, lb;
   weight_hidden_loaders(a.W, a.ldw, a.n_real, v0, a.h, a.ldh, a.scored, j0, Ts, a.H, la, lb);
   f32x16 acc[4][4];
-  zero_acc(acc);
+  if constexpr (BMODE == BIAS_NONE) zero_acc(acc);
+  else bias_acc<BMODE == BIAS_F32>(acc, a.bias, v0, a.n_real);
   dma::mainloop(la, lb, 0, a.H / dma::BKD, smem, acc);
   if (v0 + BM > a.n_real)
-    fwd_epilogue<true, BMODE>(acc, a, vt, v0, j0, Ts, smem);
+    fwd_epilogue<true>(acc, a, vt, v0, j0, Ts, smem);
   else
-    fwd_epilogue<false, BMODE>(acc, a, vt, v0, j0, Ts, smem);
+    fwd_epilogue<false>(acc, a, vt, v0, j0, Ts, smem);
 }
 
 // ------------------------------------------------------------------------------------
@@ -542,7 +547,7 @@ __device__ __forceinline__ void grad_store(const GradArgs& a, int v0, int j0, in
   }
 }
 
-template <bool TAIL, int BMODE, bool ENT>
+template <bool TAIL, bool ENT>
 __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArgs& a, int v0,
                                               int j0, int Ts, uint16_t* smem) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -572,8 +577,6 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArg
   __syncthreads();
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
-    float b[16];
-    bias16<BMODE, TAIL>(a.bias, vbase + mi * 32, lane, a.n_real, b);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
       const int tn = wn * 128 + ni * 32 + (lane & 31);
@@ -584,7 +587,7 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][4], const GradArg
         for (int u = 0; u < 4; ++u) {
           const int r = rg * 4 + u;
           const int vl = mi * 32 + mfma_row(r, lane);
-          const float x = xval<BMODE>(acc_read(acc[mi][ni][r]), b, r);
+          const float x = acc_read(acc[mi][ni][r]);
           // p = exp(z - lse) = 2^(x c1 log2(e) - lse log2(e));
           // g = (dlogp (1[v = t] - p) - dentropy p (z - E z)) / tau.
           const float p = __builtin_amdgcn_exp2f(fmaf(x, c1l, -lsel[ni]));
@@ -612,22 +615,16 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   dma::Loader la, lb;
   weight_hidden_loaders(a.W, a.ldw, a.n_real, v0, a.h, a.ldh, a.scored, j0, Ts, a.H, la, lb);
   f32x16 acc[4][4];
-  zero_acc(acc);
+  init_acc(acc, a.bias, a.bias_f32, v0, a.n_real);
   dma::mainloop(la, lb, 0, a.H / dma::BKD, smem, acc);
-  const bool tail = v0 + BM > a.n_real, ent = a.dent != nullptr;
-  const int bmode = a.bias == nullptr ? BIAS_NONE : a.bias_f32 ? BIAS_F32 : BIAS_BF16;
-#define LLP_GRAD_EPI(BM_, ENT_)                                          \
-  if (bmode == BM_ && ent == ENT_) {                                      \
-    if (tail) grad_epilogue<true, BM_, ENT_>(acc, a, v0, j0, Ts, smem);   \
-    else grad_epilogue<false, BM_, ENT_>(acc, a, v0, j0, Ts, smem);       \
+  const bool tail = v0 + BM > a.n_real;
+  if (a.dent != nullptr) {
+    if (tail) grad_epilogue<true, true>(acc, a, v0, j0, Ts, smem);
+    else grad_epilogue<false, true>(acc, a, v0, j0, Ts, smem);
+  } else {
+    if (tail) grad_epilogue<true, false>(acc, a, v0, j0, Ts, smem);
+    else grad_epilogue<false, false>(acc, a, v0, j0, Ts, smem);
   }
-  LLP_GRAD_EPI(BIAS_NONE, false)
-  LLP_GRAD_EPI(BIAS_NONE, true)
-  LLP_GRAD_EPI(BIAS_BF16, false)
-  LLP_GRAD_EPI(BIAS_BF16, true)
-  LLP_GRAD_EPI(BIAS_F32, false)
-  LLP_GRAD_EPI(BIAS_F32, true)
-#undef LLP_GRAD_EPI
 }
 
 // dhidden partials: P[split][j][n] = sum over the split's K range of G[j, k] W[k, n]
