@@ -11,7 +11,7 @@ namespace llp {
 
 // Number of fixed K (vocabulary) ranges the dhidden product is split into. Fixed, so that a
 // row's summation order never depends on the batch.
-constexpr int DH_SPLITS = 4;
+constexpr int DH_SPLITS = 2;
 constexpr int TILE = 256;  // BM = BN of every GEMM tile
 constexpr int KSTEP = 64;  // K depth of one pipelined GEMM step
 
