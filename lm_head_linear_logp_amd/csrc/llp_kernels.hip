@@ -297,8 +297,10 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
 }
 
 // ------------------------------------------------------------------------------------
-// Cross-tile combine, in vocabulary-tile order: wave w of 16 folds tiles w, w+16, ... for 64
-// rows, then one wave folds the 16 partials in order w = 0..15. With d_k = m_k - M:
+// Cross-tile combine, in vocabulary-tile order: chain c of 16 folds tiles c, c+16, ... of a row,
+// then the row's 16 chains are folded in order c = 0..15. A workgroup takes 16 rows x 16 chains
+// (thread = chain * 16 + row), so the 4096 rows of a chunk spread over 256 workgroups; the
+// arithmetic of a row does not depend on that grouping. With d_k = m_k - M:
 // S = sum_k s_k e^{d_k}, Q = sum_k e^{d_k}(q_k + s_k d_k log2 e); lse = M + ln S and
 // entropy = ln S - ln2 * Q / S. An empty shard gives lse = -inf, entropy 0, target logit 0,
 // in_range 0 and logp -inf ([top-p replay, "Changes" table]: empty vocabulary rows).
@@ -318,18 +320,25 @@ __device__ __forceinline__ void fold(float& M, float& S, float& Q, float m, floa
   M = N;
 }
 
-__global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
-  __shared__ float rm[16][64], rs[16][64], rq[16][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+constexpr int COMBINE_ROWS = 16, COMBINE_CHAINS = 16;
+
+__global__ __launch_bounds__(COMBINE_ROWS * COMBINE_CHAINS) void k_combine(CombineArgs a) {
+  __shared__ float rm[COMBINE_CHAINS][COMBINE_ROWS], rs[COMBINE_CHAINS][COMBINE_ROWS],
+      rq[COMBINE_CHAINS][COMBINE_ROWS];
+  const int r = threadIdx.x % COMBINE_ROWS, c = threadIdx.x / COMBINE_ROWS;
   const int Ts = *a.count;
-  const int j = blockIdx.x * 64 + lane;
-  if (blockIdx.x * 64 >= Ts) return;
+  const int j = blockIdx.x * COMBINE_ROWS + r;
+  if (blockIdx.x * COMBINE_ROWS >= Ts) return;
   float M = -INFINITY, S = 0.f, Q = 0.f;
   if (j < Ts) {
+    // Unrolled so that each thread has several independent loads in flight.
     float mmax = -INFINITY;
-    for (int vt = w; vt < a.nvt; vt += 16) mmax = fmaxf(mmax, a.pm[(int64_t)vt * a.pstride + j]);
+#pragma unroll 8
+    for (int vt = c; vt < a.nvt; vt += COMBINE_CHAINS)
+      mmax = fmaxf(mmax, a.pm[(int64_t)vt * a.pstride + j]);
     if (mmax != -INFINITY) {
-      for (int vt = w; vt < a.nvt; vt += 16) {
+#pragma unroll 8
+      for (int vt = c; vt < a.nvt; vt += COMBINE_CHAINS) {
         const int64_t o = (int64_t)vt * a.pstride + j;
         const float d = a.pm[o] - mmax, s = a.ps[o], q = a.pq[o];
         const float e = expf(d);
@@ -339,13 +348,13 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
       M = mmax;
     }
   }
-  rm[w][lane] = M;
-  rs[w][lane] = S;
-  rq[w][lane] = Q;
+  rm[c][r] = M;
+  rs[c][r] = S;
+  rq[c][r] = Q;
   __syncthreads();
-  if (w != 0 || j >= Ts) return;
+  if (c != 0 || j >= Ts) return;
   M = -INFINITY; S = 0.f; Q = 0.f;
-  for (int g = 0; g < 16; ++g) fold(M, S, Q, rm[g][lane], rs[g][lane], rq[g][lane]);
+  for (int g = 0; g < COMBINE_CHAINS; ++g) fold(M, S, Q, rm[g][r], rs[g][r], rq[g][r]);
   float lse, ent;
   if (M == -INFINITY || !(S > 0.f)) {
     lse = -INFINITY;
@@ -1116,7 +1125,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, int64_t T_cap, hipStream_t s) {
-  if (T_cap > 0) hipLaunchKernelGGL(k_combine, dim3(ceil_div64(T_cap, 64)), dim3(1024), 0, s, a);
+  if (T_cap > 0)
+    hipLaunchKernelGGL(k_combine, dim3(ceil_div64(T_cap, COMBINE_ROWS)),
+                       dim3(COMBINE_ROWS * COMBINE_CHAINS), 0, s, a);
   return hipGetLastError();
 }
 
