@@ -134,7 +134,8 @@ typedef struct {
  * [CUDA provider, "CUDA compatibility and launch support"]: context parallelism is row
  * ownership). Rows are independent: num_seqs/cu_seqlens describe packing and are validated
  * on the device (LLP_STATUS_LAYOUT_INVALID) but do not change any row's arithmetic.
- *   num_tokens  T >= 0 rows.
+ *   num_tokens  T >= 0 rows (llp_forward / llp_backward: at most 2^23 - 256, else
+ *               LLP_ERR_UNSUPPORTED; llp_forward_logits: below 2^31, else INVALID_ARGUMENT).
  *   cu_seqlens  int32 [num_seqs + 1] device array or NULL (num_seqs ignored when NULL).
  *   loss_mask   uint8 [T] device array (non-zero = scored) or NULL (every row scored).
  * Unscored rows are not computed; all their outputs are written as 0 and they get no
@@ -225,6 +226,7 @@ typedef struct {
  * apply temperature, return local reductions).
  *   logits        [T, local_size] this shard's local logits (logits_dtype: LLP_DTYPE_F32 or
  *                 LLP_DTYPE_BF16), row stride logits_stride elements.
+ *   num_tokens    T rows, 0 <= T < 2^31 (else LLP_ERR_INVALID_ARGUMENT).
  *   replay_ids    int64 [T, num_replay] global ids, row stride replay_stride; -1 = empty slot;
  *                 num_replay in [1, LLP_MAX_REPLAY_IDS]. Duplicates count once.
  *   processed_logprobs must be 1: replay scores processed (temperature/top-p) log-probs
@@ -318,7 +320,8 @@ LLP_API llp_status llp_forward(const llp_request* req, const llp_partials* out,
  * part = no merged entropy). Per row: lse = M + log sum_r exp(lse_r - M) over non-empty
  * shards; logp = target_logit of the first shard holding the target minus lse, or -inf
  * (LLP_STATUS_TARGET_NOT_FOUND); entropy = sum_r exp(lse_r - lse)(entropy_r + lse - lse_r).
- * loss_mask (device, may be NULL) zeroes unscored rows. out->entropy may be NULL. */
+ * loss_mask (device, may be NULL) zeroes unscored rows. out->entropy may be NULL.
+ * 0 <= num_tokens < 2^31 (else LLP_ERR_INVALID_ARGUMENT). */
 LLP_API llp_status llp_merge(int32_t world, const llp_partials* parts, int64_t num_tokens,
                              const uint8_t* loss_mask, const llp_final_out* out,
                              int32_t* status_word, void* stream);

@@ -246,7 +246,7 @@ LLP_API llp_status llp_keep_mask_replay(const llp_keep_mask_request* req,
   llp_status st = check_partition(req->vocab);
   if (st != LLP_OK) return st;
   const int64_t T = req->num_tokens;
-  LLP_CHECK(T >= 0 && T < (int64_t(1) << 40), LLP_ERR_INVALID_ARGUMENT, "num_tokens out of range");
+  LLP_CHECK(T >= 0 && T < (int64_t(1) << 31), LLP_ERR_INVALID_ARGUMENT, "num_tokens out of range");
   LLP_CHECK(req->processed_logprobs == 1, LLP_ERR_INVALID_ARGUMENT,
             "replay scores processed logprobs only (processed_logprobs must be 1)");
   LLP_CHECK(req->logits_dtype == LLP_DTYPE_F32 || req->logits_dtype == LLP_DTYPE_BF16,
@@ -444,7 +444,7 @@ LLP_API llp_status llp_merge(int32_t world, const llp_partials* parts, int64_t n
   LLP_CHECK(world >= 1 && world <= LLP_MAX_WORLD, LLP_ERR_INVALID_ARGUMENT,
             "world=%d outside [1, %d]", world, LLP_MAX_WORLD);
   LLP_CHECK(parts != nullptr && out != nullptr, LLP_ERR_INVALID_ARGUMENT, "parts/out is NULL");
-  LLP_CHECK(num_tokens >= 0 && num_tokens < (int64_t(1) << 40), LLP_ERR_INVALID_ARGUMENT,
+  LLP_CHECK(num_tokens >= 0 && num_tokens < (int64_t(1) << 31), LLP_ERR_INVALID_ARGUMENT,
             "num_tokens=%lld out of range", (long long)num_tokens);
   const bool want_ent = out->entropy != nullptr;
   if (num_tokens > 0) {
@@ -629,7 +629,7 @@ LLP_API llp_status llp_top_p_replay(const llp_topp_request* req, const llp_parti
   llp_status st = check_partition(req->vocab);
   if (st != LLP_OK) return st;
   const int64_t T = req->num_tokens;
-  LLP_CHECK(T >= 0 && T < (int64_t(1) << 40), LLP_ERR_INVALID_ARGUMENT, "num_tokens out of range");
+  LLP_CHECK(T >= 0 && T < (int64_t(1) << 31), LLP_ERR_INVALID_ARGUMENT, "num_tokens out of range");
   LLP_CHECK(req->processed_logprobs == 1, LLP_ERR_INVALID_ARGUMENT,
             "top-p replay scores processed logprobs only (processed_logprobs must be 1)");
   LLP_CHECK(req->num_replay >= 1 && req->num_replay <= LLP_MAX_REPLAY_IDS,

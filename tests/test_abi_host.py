@@ -220,6 +220,8 @@ def test_merge_validation():
     # entropy requested but a part has none
     assert _merge(2, [p, p], out=A.llp_final_out(FAKE, FAKE, FAKE)) == A.LLP_ERR_INVALID_ARGUMENT
     assert _merge(1, [p], out=A.llp_final_out(None, FAKE, None)) == A.LLP_ERR_INVALID_ARGUMENT
+    # more rows than one launch grid covers
+    assert _merge(1, [p], T=1 << 31) == A.LLP_ERR_INVALID_ARGUMENT
 
 
 def good_topp():
@@ -243,6 +245,8 @@ BAD_TOPP = [
     ("tau zero", lambda q: setattr(q, "temperature", 0.0)),
     ("ids NULL", lambda q: setattr(q, "replay_ids", None)),
     ("bad partition", lambda q: setattr(q.vocab, "real_vocab", 200000)),
+    ("T = 2^31 (grid limit)", lambda q: setattr(q, "num_tokens", 1 << 31)),
+    ("T < 0", lambda q: setattr(q, "num_tokens", -1)),
 ]
 
 
@@ -323,6 +327,7 @@ BAD_LOGITS = [
     ("unknown flag", lambda r: setattr(r, "flags", 4)),
     ("targets NULL", lambda r: setattr(r, "target_ids", None)),
     ("real > padded", lambda r: setattr(r.vocab, "real_vocab", 2000)),
+    ("T = 2^31 (grid limit)", lambda r: setattr(r.layout, "num_tokens", 1 << 31)),
 ]
 
 
@@ -362,6 +367,7 @@ BAD_KEEP = [
     ("dtype", lambda r: setattr(r, "logits_dtype", 0)),
     ("tau nan", lambda r: setattr(r, "temperature", float("nan"))),
     ("keep NULL", lambda r: setattr(r, "keep_mask", None)),
+    ("T = 2^31 (grid limit)", lambda r: setattr(r, "num_tokens", 1 << 31)),
 ]
 
 
