@@ -6,7 +6,9 @@ targets sampled from the fp64 softmax, stored under tests/golden):
   1. llp_forward   -- layout/mask indexing, fused bf16 MFMA GEMM + online max/sum-exp/
                       target/entropy epilogue, fixed-order cross-tile combine;
   2. llp_merge     -- rank-ordered merge of the shard partials (here one shard);
-  3. llp_backward  -- gradient recompute G (bf16), dhidden = G W, dweight += G^T h;
+  3. llp_backward  -- gradient recompute G (bf16), dhidden = G W, dweight = G^T h
+                      (LLP_FLAG_OVERWRITE_GRADS: the step's one batch is its whole
+                      gradient; the accumulate form, dweight += G^T h, is timed apart);
   4. llp_top_p_replay x 4 shards + llp_merge -- compact top-p replay scoring of 4096 rows of
                       fp32 logits [4096, 151936] with <= 64 candidate ids per row.
 Inputs are resident in HBM before the timed region. The value is scored tokens/s of the
@@ -264,7 +266,7 @@ def main():
     rtg = torch.from_numpy(tp["targets"]).cuda()
     del tp
     shards = synth.shard_ranges()
-    dW = torch.zeros((VP, H), dtype=torch.float32, device="cuda")
+    dW = torch.empty((VP, H), dtype=torch.float32, device="cuda")
     dH = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -278,7 +280,7 @@ def main():
         mg = llp.merge([out])
         if e: e[2].record(stream)
         llp.backward(h, W, tg, mg["lse"], dlogp, temperature=TAU, real_vocab=VR, padded_vocab=VP,
-                     dweight=dW, dhidden=dH)
+                     dweight=dW, dhidden=dH, overwrite=True)
         if e: e[3].record(stream)
         parts = [llp.top_p_replay(logits[:, off:off + n], rids, rtg, temperature=TAU, offset=off,
                                   real_vocab=VR, padded_vocab=VP, rank=r, world=4)
@@ -308,8 +310,23 @@ def main():
     total_ms = float(events[0][0].elapsed_time(events[-1][4]))
     ms_per_step = total_ms / args.steps
     fwd_ms, merge_ms, bwd_ms, topp_ms = (float(x) for x in ph.mean(axis=0))
+    # The accumulate form of the backward (dweight += G^T h, what the later chunks of a step
+    # run), after the timed steps, on the same inputs.
+    mg = llp.merge([llp.forward(h, W, tg, temperature=TAU, real_vocab=VR, padded_vocab=VP)])
+    ea = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    llp.backward(h, W, tg, mg["lse"], dlogp, temperature=TAU, real_vocab=VR, padded_vocab=VP,
+                 dweight=dW, dhidden=dH)
+    ea[0].record(stream)
+    for _ in range(5):
+        llp.backward(h, W, tg, mg["lse"], dlogp, temperature=TAU, real_vocab=VR,
+                     padded_vocab=VP, dweight=dW, dhidden=dH)
+    ea[1].record(stream)
+    torch.cuda.synchronize()
+    bwd_acc_ms = float(ea[0].elapsed_time(ea[1])) / 5
+    del mg
     log(f"phases (ms): forward {fwd_ms:.3f} merge {merge_ms:.3f} backward {bwd_ms:.3f} "
-        f"top-p {topp_ms:.3f}; step {ms_per_step:.3f} (host wall {1e3 * wall / args.steps:.3f})")
+        f"top-p {topp_ms:.3f}; step {ms_per_step:.3f} (host wall {1e3 * wall / args.steps:.3f}); "
+        f"backward with dweight accumulated {bwd_acc_ms:.3f}")
 
     flop_fwd = 2.0 * T * H * VR
     ach_fwd = flop_fwd / (fwd_ms * 1e-3) / 1e12
@@ -342,6 +359,9 @@ def main():
                       "top_p_4shards_plus_merge": topp_ms},
         "forward_tokens_per_s": T / (fwd_ms * 1e-3),
         "backward_tflops": ach_bwd,
+        "backward_accumulate": {"ms": bwd_acc_ms, "tflops": flop_bwd / (bwd_acc_ms * 1e-3) / 1e12,
+                                "what": "llp_backward with dweight += G^T h (later chunks of a "
+                                        "step), 5 calls after the timed steps"},
         "forward_backward_tflops": (flop_fwd + flop_bwd) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12,
         "top_p": {"us": topp_ms * 1e3, "algorithmic_bytes": topp_bytes,
                   "GBps": topp_bytes / (topp_ms * 1e-3) / 1e9, "peak_GBps": PEAK_HBM_GBS},

@@ -75,7 +75,13 @@ enum {
 
 enum { LLP_DTYPE_BF16 = 1, LLP_DTYPE_F32 = 2 };
 enum { LLP_OP_FORWARD = 1, LLP_OP_BACKWARD = 2 };
-enum { LLP_FLAG_WANT_ENTROPY = 1 };
+/* Request flags.
+ *   LLP_FLAG_WANT_ENTROPY     the forward also computes the entropy.
+ *   LLP_FLAG_OVERWRITE_GRADS  llp_backward writes dweight and dbias (= this call's gradient,
+ *                             padding rows 0) instead of adding to them: the first chunk of a
+ *                             step needs no zeroed buffer and no read of one. Ignored by
+ *                             llp_forward. */
+enum { LLP_FLAG_WANT_ENTROPY = 1, LLP_FLAG_OVERWRITE_GRADS = 2 };
 
 /* Library identity and route evidence ([CUDA provider, "Changes"]: validation of identity;
  * native/provider route evidence). */
@@ -154,7 +160,7 @@ typedef struct {
  *   temperature  finite, > 0. Logits are z = (hidden . weight^T + bias) * fl32(1/temperature):
  *                temperature is applied exactly once ([ROCm provider, "Megatron
  *                integration"]; [top-p replay, "Summary"]).
- *   flags        LLP_FLAG_WANT_ENTROPY.
+ *   flags        LLP_FLAG_WANT_ENTROPY, LLP_FLAG_OVERWRITE_GRADS.
  *   status_word  int32 device word OR-ed with LLP_STATUS_* bits, or NULL. */
 typedef struct {
   llp_projection proj;
@@ -208,8 +214,12 @@ typedef struct {
  *            sums the shards' dhidden.
  *   dweight  fp32 [local_size, H], row stride dweight_stride (>= H, multiple of 4, < 2^21,
  *            else INVALID_ARGUMENT / UNSUPPORTED), 16-byte aligned base: ACCUMULATED (+=) with
- *            G^T . hidden over this call's rows; padding rows untouched.
- *   dbias    fp32 [local_size] ACCUMULATED, or NULL.
+ *            G^T . hidden over this call's rows; padding rows untouched. With
+ *            LLP_FLAG_OVERWRITE_GRADS: OVERWRITTEN with G^T . hidden, padding rows (and every
+ *            row of a call with no rows) written as 0; bitwise the accumulate form applied
+ *            to a zeroed buffer.
+ *   dbias    fp32 [local_size] ACCUMULATED (OVERWRITTEN with LLP_FLAG_OVERWRITE_GRADS), or
+ *            NULL.
  * G[t, v] = (dlogp_t (1[v = target_t] - p_tv) - dentropy_t p_tv (z_tv - E_p z_t)) / temperature
  * with p = exp(z - lse), is rounded to bf16 once and feeds all three products. */
 typedef struct {
@@ -327,7 +337,7 @@ LLP_API llp_status llp_merge(int32_t world, const llp_partials* parts, int64_t n
                              int32_t* status_word, void* stream);
 
 /* Backward for one shard: dhidden = G . weight (overwrite), dweight += G^T . hidden,
- * dbias += sum_t G (gradients must flow: [CUDA provider, "Motivation"], strict mode rejects
+ * dbias += sum_t G (= instead of += with LLP_FLAG_OVERWRITE_GRADS) (gradients must flow: [CUDA provider, "Motivation"], strict mode rejects
  * detached gradients). Needs the merged lse of every scored row. */
 LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
                                 const llp_bwd_out* out, void* workspace,

@@ -217,12 +217,16 @@ def backward(hidden: torch.Tensor, weight: torch.Tensor, target_ids: torch.Tenso
              entropy: Optional[torch.Tensor] = None, dweight: Optional[torch.Tensor] = None,
              dbias: Optional[torch.Tensor] = None, want_dbias: Optional[bool] = None,
              dhidden: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None) -> dict:
+             workspace: Optional[torch.Tensor] = None, overwrite: bool = False) -> dict:
     """llp_backward on one shard: dhidden (bf16, overwritten), dweight (fp32, accumulated),
-    dbias (fp32, accumulated; allocated when the request has a bias or want_dbias)."""
+    dbias (fp32, accumulated; allocated when the request has a bias or want_dbias). With
+    overwrite=True (LLP_FLAG_OVERWRITE_GRADS) dweight and dbias are written instead of added
+    to, and a missing dweight/dbias is allocated uninitialised."""
     open(hidden.device.index)
     req = _request(hidden, weight, target_ids, temperature, bias, loss_mask, cu_seqlens, offset,
                    real_vocab, padded_vocab, rank, world, False, status)
+    if overwrite:
+        req.flags |= A.LLP_FLAG_OVERWRITE_GRADS
     dev = hidden.device
     T, H = hidden.shape
     for name, t in (("lse", lse), ("dlogp", dlogp)):
@@ -232,14 +236,15 @@ def backward(hidden: torch.Tensor, weight: torch.Tensor, target_ids: torch.Tenso
         _need(entropy, "entropy", torch.float32, 1, dev)
     if dhidden is None:
         dhidden = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    alloc = torch.empty if overwrite else torch.zeros
     if dweight is None:
-        dweight = torch.zeros(weight.shape, dtype=torch.float32, device=dev)
+        dweight = alloc(weight.shape, dtype=torch.float32, device=dev)
     _need(dhidden, "dhidden", torch.bfloat16, 2, dev)
     _need(dweight, "dweight", torch.float32, 2, dev)
     if want_dbias is None:
         want_dbias = bias is not None
     if dbias is None and want_dbias:
-        dbias = torch.zeros(weight.shape[0], dtype=torch.float32, device=dev)
+        dbias = alloc(weight.shape[0], dtype=torch.float32, device=dev)
     bi = A.llp_bwd_in(_ptr(lse), _ptr(dlogp), _ptr(dentropy), _ptr(entropy))
     bo = A.llp_bwd_out(_ptr(dhidden), dhidden.stride(0) if T > 0 else H, _ptr(dweight),
                        dweight.stride(0) if weight.shape[0] > 0 else H, _ptr(dbias))

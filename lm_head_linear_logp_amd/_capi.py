@@ -23,6 +23,7 @@ LLP_DTYPE_F32 = 2
 LLP_OP_FORWARD = 1
 LLP_OP_BACKWARD = 2
 LLP_FLAG_WANT_ENTROPY = 1
+LLP_FLAG_OVERWRITE_GRADS = 2
 LLP_MAX_REPLAY_IDS = 64
 LLP_MAX_WORLD = 64
 

@@ -108,8 +108,8 @@ llp_status check_request(const llp_request* req) {
   }
   LLP_CHECK(isfinite(req->temperature) && req->temperature > 0.f, LLP_ERR_INVALID_ARGUMENT,
             "temperature must be finite and > 0");
-  LLP_CHECK((req->flags & ~uint32_t(LLP_FLAG_WANT_ENTROPY)) == 0, LLP_ERR_INVALID_ARGUMENT,
-            "unknown flags 0x%x", req->flags);
+  LLP_CHECK((req->flags & ~uint32_t(LLP_FLAG_WANT_ENTROPY | LLP_FLAG_OVERWRITE_GRADS)) == 0,
+            LLP_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", req->flags);
   if (req->layout.cu_seqlens != nullptr)
     LLP_CHECK(req->layout.num_seqs >= 0, LLP_ERR_INVALID_ARGUMENT, "num_seqs < 0");
   return LLP_OK;
@@ -510,8 +510,26 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
             "workspace must be non-NULL and 256-byte aligned");
   st = check_device();
   if (st != LLP_OK) return st;
-  if (T == 0) return LLP_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool overwrite = (req->flags & LLP_FLAG_OVERWRITE_GRADS) != 0;
+  // Overwrite mode: rows the products do not write (padding rows; every row when the call has
+  // no rows) are written as 0.
+  if (overwrite) {
+    ZeroArgs za{};
+    za.p = out->dweight;
+    za.ld = out->dweight_stride;
+    za.r0 = T == 0 ? 0 : n_real;
+    za.r1 = req->vocab.local_size;
+    za.cols = H;
+    LLP_HIP(launch_zero_rows(za, s), "zero kernel launch");
+    if (out->dbias != nullptr) {
+      za.p = out->dbias;
+      za.ld = 1;
+      za.cols = 1;
+      LLP_HIP(launch_zero_rows(za, s), "zero kernel launch");
+    }
+  }
+  if (T == 0) return LLP_OK;
 
   LayoutArgs la{};
   la.T = T;
@@ -598,6 +616,7 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
     wa.count = la.count;
     wa.dW = out->dweight;
     wa.lddw = out->dweight_stride;
+    wa.overwrite = overwrite;
     LLP_HIP(launch_dw(wa, s), "dweight kernel launch");
 
     if (out->dbias != nullptr) {
@@ -607,6 +626,7 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
       ba.n_real = n_real;
       ba.count = la.count;
       ba.db = out->dbias;
+      ba.overwrite = overwrite;
       LLP_HIP(launch_dbias(ba, s), "dbias kernel launch");
     }
   }

@@ -201,6 +201,14 @@ struct DwArgs {
   const int32_t* count;
   float* dW;
   int64_t lddw;
+  int32_t overwrite;  // 1: dW = the product (no read of dW); 0: dW += the product
+};
+
+struct ZeroArgs {
+  float* p;
+  int64_t ld;
+  int64_t r0, r1;  // rows [r0, r1)
+  int64_t cols;
 };
 
 struct TransposeArgs {
@@ -220,6 +228,7 @@ struct DbArgs {
   int64_t n_real;
   const int32_t* count;
   float* db;
+  int32_t overwrite;  // 1: db = the sum; 0: db += the sum
 };
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
@@ -233,6 +242,7 @@ hipError_t launch_dh_reduce(const DhReduceArgs& a, hipStream_t s);
 hipError_t launch_dw(const DwArgs& a, hipStream_t s);
 hipError_t launch_transpose(const TransposeArgs& a, int64_t rows, hipStream_t s);
 hipError_t launch_dbias(const DbArgs& a, hipStream_t s);
+hipError_t launch_zero_rows(const ZeroArgs& a, hipStream_t s);
 hipError_t launch_logits(const LogitsArgs& a, hipStream_t s);
 hipError_t launch_keep(const KeepArgs& a, hipStream_t s);
 hipError_t probe_kernels();

@@ -770,46 +770,82 @@ __device__ __forceinline__ void dw_add_store(const f32x16 (&acc)[4][4], const Dw
     }
 }
 
+// Every chunk of the tile written with its sum (overwrite mode): no old values are read.
+__device__ __forceinline__ void dw_store(const f32x16 (&acc)[4][4], const DwTile& t, float* base) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = __builtin_bit_cast(uint32_t, acc_read(acc[mi][ni][4 * q + e]));
+        const uint32_t off = t.off[mi][ni][q];
+        if (off != DW_MASKED)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(base) + off) = o;
+      }
+}
+
 // dweight[v, n] += sum_j G[j, v] hgT[n, j] over the scored rows j in ascending order
-// (G and hgT are zero from the count up to the next whole K step).
+// (G and hgT are zero from the count up to the next whole K step). OVERWRITE: dweight[v, n] =
+// that sum instead, written as +0 when no row is scored (a sum that starts at +0 is never -0,
+// so this is bitwise the accumulate form applied to a zeroed dweight).
+template <bool OVERWRITE>
 __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dw(DwArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
   int mt, nt;
   vocab_token_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntm, a.ntn, mt, nt);
   const int Ts = *a.count;
-  if (Ts <= 0) return;
+  if (!OVERWRITE && Ts <= 0) return;
   const int m0 = mt * BM, n0 = nt * BN;
-  // A (tile rows): hgT rows n0 .. (< H), K = scored rows rounded up to whole steps.
-  // B (tile columns): G itself, K-major: rows = scored rows (zero from the count to the next
-  // whole step), columns m0 .. m0+255 (inside the padded vocabulary capacity).
-  const int nn = a.H - n0 < BN ? a.H - n0 : BN;
-  const int nk = (Ts + dma::BKD - 1) / dma::BKD;
-  const int64_t kb = (int64_t)nk * dma::BKD;
-  dma::Loader la;
-  la.init(a.hgT + (int64_t)n0 * a.ldk, (uint64_t)((nn - 1) * a.ldk + kb) * 2);
-#pragma unroll
-  for (int u = 0; u < dma::NI; ++u) {
-    const int r = dma::Loader::row_of(u);
-    la.set(u, r < nn ? r : nn - 1, a.ldk);
-  }
-  dma::LoaderK lb;
-  lb.init(a.G + m0, a.ldg, (int)kb - 1, BM);
   DwTile t;
   dw_tile_setup(a, m0, n0, t);
   float* dwt = a.dW + (int64_t)m0 * a.lddw + n0;
   f32x16 acc[4][4];
   zero_acc(acc);
-  dma::mainloop(la, lb, 0, nk, smem, acc);
-  // Two block rows of old values in flight at a time.
-  u32x4 v0[16], v1[16];
-  dw_load(t, dwt, 0, v0);
-  dw_load(t, dwt, 1, v1);
-  dw_add_store(acc, t, dwt, 0, v0);
-  dw_load(t, dwt, 2, v0);
-  dw_add_store(acc, t, dwt, 1, v1);
-  dw_load(t, dwt, 3, v1);
-  dw_add_store(acc, t, dwt, 2, v0);
-  dw_add_store(acc, t, dwt, 3, v1);
+  if (Ts > 0) {
+    // A (tile rows): hgT rows n0 .. (< H), K = scored rows rounded up to whole steps.
+    // B (tile columns): G itself, K-major: rows = scored rows (zero from the count to the next
+    // whole step), columns m0 .. m0+255 (inside the padded vocabulary capacity).
+    const int nn = a.H - n0 < BN ? a.H - n0 : BN;
+    const int nk = (Ts + dma::BKD - 1) / dma::BKD;
+    const int64_t kb = (int64_t)nk * dma::BKD;
+    dma::Loader la;
+    la.init(a.hgT + (int64_t)n0 * a.ldk, (uint64_t)((nn - 1) * a.ldk + kb) * 2);
+#pragma unroll
+    for (int u = 0; u < dma::NI; ++u) {
+      const int r = dma::Loader::row_of(u);
+      la.set(u, r < nn ? r : nn - 1, a.ldk);
+    }
+    dma::LoaderK lb;
+    lb.init(a.G + m0, a.ldg, (int)kb - 1, BM);
+    dma::mainloop(la, lb, 0, nk, smem, acc);
+  }
+  if constexpr (OVERWRITE) {
+    dw_store(acc, t, dwt);
+  } else {
+    // Two block rows of old values in flight at a time.
+    u32x4 v0[16], v1[16];
+    dw_load(t, dwt, 0, v0);
+    dw_load(t, dwt, 1, v1);
+    dw_add_store(acc, t, dwt, 0, v0);
+    dw_load(t, dwt, 2, v0);
+    dw_add_store(acc, t, dwt, 1, v1);
+    dw_load(t, dwt, 3, v1);
+    dw_add_store(acc, t, dwt, 2, v0);
+    dw_add_store(acc, t, dwt, 3, v1);
+  }
+}
+
+// p[r * ld + c] = 0 for rows r0 <= r < r1 and columns c < cols (grid-stride, one float per
+// thread and pass): padding rows of dweight/dbias, or all of them for a call with no rows, in
+// overwrite mode.
+__global__ __launch_bounds__(256) void k_zero_rows(ZeroArgs a) {
+  const int64_t n = (a.r1 - a.r0) * a.cols;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    a.p[(a.r0 + i / a.cols) * a.ld + i % a.cols] = 0.f;
 }
 
 // out[c][r] = in[row(r)][c] for r < nvalid (zero for nvalid <= r < the grid's rows), 64 x 64
@@ -847,14 +883,14 @@ __global__ __launch_bounds__(256) void k_transpose(TransposeArgs a) {
   }
 }
 
-// dbias[v] += sum_j G[j, v] over scored rows in order.
+// dbias[v] += sum_j G[j, v] over scored rows in order (overwrite: dbias[v] = the sum).
 __global__ __launch_bounds__(256) void k_dbias(DbArgs a) {
   const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (v >= a.n_real) return;
   const int Ts = *a.count;
   float s = 0.f;
   for (int j = 0; j < Ts; ++j) s += bf16_to_f32(a.G[(int64_t)j * a.ldg + v]);
-  a.db[v] += s;
+  a.db[v] = a.overwrite ? s : a.db[v] + s;
 }
 
 // ------------------------------------------------------------------------------------
@@ -1160,7 +1196,20 @@ hipError_t launch_dh_reduce(const DhReduceArgs& a, hipStream_t s) {
 
 hipError_t launch_dw(const DwArgs& a, hipStream_t s) {
   const int n = a.ntm * a.ntn;
-  if (n > 0) hipLaunchKernelGGL(k_dw, dim3(n), dim3(NTHREADS), 0, s, a);
+  if (n > 0) {
+    if (a.overwrite) hipLaunchKernelGGL(k_dw<true>, dim3(n), dim3(NTHREADS), 0, s, a);
+    else hipLaunchKernelGGL(k_dw<false>, dim3(n), dim3(NTHREADS), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_rows(const ZeroArgs& a, hipStream_t s) {
+  const int64_t n = (a.r1 - a.r0) * a.cols;
+  if (n > 0) {
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(k_zero_rows, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256),
+                       0, s, a);
+  }
   return hipGetLastError();
 }
 

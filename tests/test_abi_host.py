@@ -74,7 +74,7 @@ def test_header_constants_match():
                  "LLP_STATUS_REPLAY_ID_INVALID", "LLP_STATUS_LAYOUT_INVALID",
                  "LLP_ERR_UNAVAILABLE", "LLP_ERR_INVALID_ARGUMENT", "LLP_ERR_UNSUPPORTED",
                  "LLP_DTYPE_BF16", "LLP_DTYPE_F32", "LLP_OP_FORWARD", "LLP_OP_BACKWARD",
-                 "LLP_FLAG_WANT_ENTROPY"):
+                 "LLP_FLAG_WANT_ENTROPY", "LLP_FLAG_OVERWRITE_GRADS"):
         assert int(re.search(rf"\b{name} = (\d+)", src).group(1)) == getattr(A, name), name
 
 
@@ -146,7 +146,7 @@ BAD_FORWARD = [
     ("world too big", lambda r: setattr(r.vocab, "world", 65), A.LLP_ERR_INVALID_ARGUMENT),
     ("bad bias dtype", lambda r: (setattr(r.proj, "bias", FAKE), setattr(r.proj, "bias_dtype", 7)),
      A.LLP_ERR_INVALID_ARGUMENT),
-    ("unknown flag", lambda r: setattr(r, "flags", 2), A.LLP_ERR_INVALID_ARGUMENT),
+    ("unknown flag", lambda r: setattr(r, "flags", 4), A.LLP_ERR_INVALID_ARGUMENT),
     ("T too large", lambda r: setattr(r.layout, "num_tokens", 1 << 23), A.LLP_ERR_UNSUPPORTED),
     ("hidden bytes > 4 GiB", lambda r: (setattr(r.layout, "num_tokens", 1 << 20),
                                         setattr(r.proj, "hidden_stride", 4096)), A.LLP_ERR_UNSUPPORTED),
@@ -281,6 +281,23 @@ def test_backward_validation():
     bo.dweight = FAKE
     bi.lse = None
     assert call() == A.LLP_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.skipif(_gpu_present(), reason="a GPU is present")
+def test_backward_overwrite_flag_passes_validation():
+    """LLP_FLAG_OVERWRITE_GRADS is a known request flag: a backward request carrying it gets
+    past validation (without a device it then fails in llp_open's check); flag 4 is unknown."""
+    lib = A.load()
+    r = good_request()
+    bi = A.llp_bwd_in(FAKE, FAKE, None, None)
+    bo = A.llp_bwd_out(FAKE, 4096, FAKE, 4096, None)
+    call = lambda: lib.llp_backward(C.byref(r), C.byref(bi), C.byref(bo), FAKE, 1 << 40, None)
+    r.flags = A.LLP_FLAG_OVERWRITE_GRADS
+    st = call()
+    assert st != A.LLP_ERR_INVALID_ARGUMENT or "llp_open" in lib.llp_last_error().decode()
+    r.flags = 4
+    assert call() == A.LLP_ERR_INVALID_ARGUMENT
+    assert b"unknown flags" in lib.llp_last_error()
 
 
 def test_backward_rejects_bad_dweight_layout():

@@ -449,3 +449,52 @@ def test_backward_f32_bias_masked_and_empty(llp):
                         dweight=ones_w, dbias=ones_b)
     assert out0["dhidden"].numel() == 0
     assert np.all(host(ones_w) == 1) and np.all(host(ones_b) == 1)
+
+
+def test_backward_overwrite_mode(llp):
+    """LLP_FLAG_OVERWRITE_GRADS: dweight and dbias are bitwise the accumulate form applied to
+    zeroed buffers, whatever the buffers held (NaN here), and match the oracle; padding rows
+    are written as 0. All rows masked, no rows at all, and a shard of padding only: every row
+    of dweight and dbias is written as 0."""
+    T, H, Vr, Vp, tau = 300, 320, 1300, 1536, 0.8
+    case = synth.small_case(T, H, Vr, Vp, tau, case_id=74, mask_frac=0.25, with_bias=True,
+                            w_std=0.1)
+    f = oracle.forward(case["hidden"], case["weight"], case["bias"], tau, case["targets"],
+                       case["mask"], Vr)
+    dlogp = synth.rng(74, 3).standard_normal(T) * case["mask"]
+    ref = oracle.backward(case["hidden"], case["weight"], case["bias"], tau, case["targets"],
+                          case["mask"], 0, Vp, Vr, f["lse"], dlogp)
+    acc = run_backward(llp, case, f["lse"], dlogp, bias_dtype=torch.float32)
+    nan_w = torch.full((Vp, H), float("nan"), dtype=torch.float32, device="cuda")
+    nan_b = torch.full((Vp,), float("nan"), dtype=torch.float32, device="cuda")
+    ow = run_backward(llp, case, f["lse"], dlogp, bias_dtype=torch.float32, dweight=nan_w,
+                      dbias=nan_b, overwrite=True)
+    assert bytes_equal(ow["dweight"], acc["dweight"]) and bytes_equal(ow["dbias"], acc["dbias"])
+    assert bytes_equal(ow["dhidden"], acc["dhidden"])
+    r2 = normwise_rel(host(nan_w), ref["dweight"])
+    r3 = normwise_rel(host(nan_b), ref["dbias"])
+    say(f"overwrite: rel dW {r2:.2e} db {r3:.2e}")
+    assert r2 <= GRAD_RTOL and r3 <= GRAD_RTOL
+    assert np.all(host(nan_w)[Vr:] == 0) and np.all(host(nan_b)[Vr:] == 0)
+
+    def all_zero(*ts):
+        return all(np.all(host(t) == 0) for t in ts)
+
+    for name, c, lse, dl in (
+            ("all rows masked", dict(case, mask=np.zeros(T, np.uint8)), f["lse"], dlogp),
+            ("no rows", dict(case, hidden=case["hidden"][:0], targets=case["targets"][:0],
+                             mask=case["mask"][:0]), f["lse"][:0], dlogp[:0])):
+        say(f"overwrite: {name}")
+        nan_w.fill_(float("nan"))
+        nan_b.fill_(float("nan"))
+        run_backward(llp, c, lse, dl, bias_dtype=torch.float32, dweight=nan_w, dbias=nan_b,
+                     overwrite=True)
+        assert all_zero(nan_w, nan_b), name
+    say("overwrite: padding-only shard")
+    lo = Vr
+    sw = torch.full((Vp - lo, H), float("nan"), dtype=torch.float32, device="cuda")
+    sb = torch.full((Vp - lo,), float("nan"), dtype=torch.float32, device="cuda")
+    out = run_backward(llp, dict(case, weight=case["weight"][lo:], bias=case["bias"][lo:]),
+                       f["lse"], dlogp, bias_dtype=torch.float32, offset=lo, rank=1, world=2,
+                       dweight=sw, dbias=sb, overwrite=True)
+    assert all_zero(sw, sb, out["dhidden"])
