@@ -422,100 +422,150 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
 // ------------------------------------------------------------------------------------
 // Compact top-p replay scorer ([top-p replay, "Summary"] and "Changes" table: validate the
 // replay inputs, sort and deduplicate up to 64 ids, apply temperature, return local
-// reductions; score the compact ids directly, no full-vocabulary keep mask). One wave64 per
-// row: lane k holds slot k; ids inside the shard's real range become local keys, the rest a
-// sentinel; a bitonic sort across lanes, adjacent dedup, and compaction by ballot put the
-// i-th distinct id on lane i, so the fixed butterfly sum is independent of the order and
-// multiplicity of the listed ids.
+// reductions; score the compact ids directly, no full-vocabulary keep mask). A wave64 per
+// row (or per few rows): lane k holds slot k; ids inside the shard's real range become local keys, the rest a
+// sentinel. The c keys are first packed into lanes 0..c-1 (in slot order), then a bitonic
+// sort over the first P = 2^ceil(log2 c) lanes (the lanes past c hold the sentinel, the
+// largest key, so they already sit in sorted position), adjacent dedup and compaction by
+// ballot put the i-th distinct id on lane i: the fixed butterfly sum is independent of the
+// order and multiplicity of the listed ids. A shard holds a handful of a nucleus's ids, so P
+// is small and the sort takes a few stages instead of the 21 of a 64-lane network.
 // ------------------------------------------------------------------------------------
 // Scores a set of logits held one per lane in ascending-id order (lane i holds the i-th
 // distinct id's z when `live`, else -inf): M = max, returns sum exp(z - M), both by a fixed
 // butterfly, so the result is a function of the set alone. The compact and the dense
 // keep-mask scorers both end here, which makes them bitwise equal on the same nucleus.
-__device__ __forceinline__ float wave_set_sum(float z, bool live, float& M) {
+// `span` (a power of two in 1..64, wave-uniform) bounds the live lanes: they are all below
+// it. The butterfly steps with off >= span only combine lane l < span with lanes whose values
+// are -inf (max) and 0 (sum), which leaves lane l's value unchanged, so skipping them gives
+// lanes below span, lane 0 included, the bits of the full 64-lane butterfly. Lanes at or
+// past span return garbage; callers use lane 0.
+__device__ __forceinline__ float wave_set_sum(float z, bool live, float& M, int span) {
   M = z;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  for (int off = span >> 1; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float e = live ? expf(z - M) : 0.f;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) e += __shfl_xor(e, off);
+  for (int off = span >> 1; off > 0; off >>= 1) e += __shfl_xor(e, off);
   return e;
 }
 
+// Smallest power of two >= n (1 for n <= 1), n <= 64.
+__device__ __forceinline__ int pow2_ceil(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// A wave scores RPW consecutive rows: every row's loads (ids, target, mask) are issued first,
+// and later every row's logit gathers, so a wave waits two memory latencies per RPW rows;
+// each row's arithmetic is the one-row arithmetic.
+template <int RPW>
 __global__ __launch_bounds__(256) void k_topp(ToppArgs a) {
-  __shared__ float zs[4][64];
+  __shared__ float zs[4][RPW][64];
+  __shared__ int ks[4][RPW][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * 4 + w;
-  if (row >= a.T) return;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + w) * RPW;
+  if (row0 >= a.T) return;
+  const int nr = a.T - row0 < RPW ? (int)(a.T - row0) : RPW;
   int status = 0;
-  int64_t id = -1;
-  if (lane < a.K) id = a.ids[row * a.ids_stride + lane];
-  if (id < -1 || id >= a.real_vocab) {
-    status |= LLP_STATUS_REPLAY_ID_INVALID;
-    id = -1;
-  }
-  const bool scored = a.mask == nullptr || a.mask[row] != 0;
-  if (!scored) {
-    if (lane == 0) {
-      a.out_t[row] = 0.f;
-      a.out_f[row] = 0;
-      a.out_l[row] = 0.f;
-      if (a.out_p) a.out_p[row] = 0.f;
-    }
-    if (status && a.status) atomicOr(a.status, status);
-    return;
-  }
-  const int64_t loc = id - a.offset;
-  int key = (id >= 0 && loc >= 0 && loc < a.n_real) ? (int)loc : 0x7FFFFFFF;
-  // Bitonic sort, ascending over lane index.
+  // A row past T repeats the last row: read, never written.
+  int64_t id[RPW], tg[RPW];
+  bool scored[RPW];
 #pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
+  for (int r = 0; r < RPW; ++r) {
+    const int64_t row = row0 + (r < nr ? r : nr - 1);
+    id[r] = lane < a.K ? a.ids[row * a.ids_stride + lane] : -1;
+    tg[r] = a.targets[row];
+    scored[r] = r < nr && (a.mask == nullptr || a.mask[row] != 0);
+  }
+  int key[RPW];
 #pragma unroll
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      const int other = __shfl_xor(key, jj);
-      const bool up = (lane & k) == 0;
-      const bool lower = (lane & jj) == 0;
-      const int lo = min(key, other), hi = max(key, other);
-      key = (lower == up) ? lo : hi;
+  for (int r = 0; r < RPW; ++r) {
+    int64_t v = id[r];
+    if (v < -1 || v >= a.real_vocab) {
+      if (r < nr) status |= LLP_STATUS_REPLAY_ID_INVALID;
+      v = -1;
+    }
+    const int64_t loc = v - a.offset;
+    const bool in_shard = scored[r] && v >= 0 && loc >= 0 && loc < a.n_real;
+    // Pack the in-shard keys into lanes 0..c-1 (ks[w] is private to this wave; one wave's
+    // LDS accesses complete in issue order).
+    const uint64_t vb = __builtin_amdgcn_ballot_w64(in_shard);
+    const int c = __popcll(vb);
+    if (in_shard)
+      ks[w][r][__builtin_amdgcn_mbcnt_hi((uint32_t)(vb >> 32),
+                                         __builtin_amdgcn_mbcnt_lo((uint32_t)vb, 0))] = (int)loc;
+    __builtin_amdgcn_wave_barrier();
+    int k0 = lane < c ? ks[w][r][lane] : 0x7FFFFFFF;
+    // Bitonic sort of lanes 0..P-1, ascending; the partners of lane l (l ^ jj, jj < P) stay in
+    // its block of P lanes, which past lane c holds sentinels only.
+    const int P = pow2_ceil(c);
+    for (int k = 2; k <= P; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        const int other = __shfl_xor(k0, jj);
+        const bool up = (lane & k) == 0;
+        const bool lower = (lane & jj) == 0;
+        const int lo = min(k0, other), hi = max(k0, other);
+        k0 = (lower == up) ? lo : hi;
+      }
+    }
+    key[r] = k0;
+  }
+  // Dedup and compaction; the gathers of every row's distinct logits go out together.
+  uint64_t bal[RPW], tb[RPW];
+  float x[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int prev = __shfl_up(key[r], 1);
+    const bool keep = key[r] != 0x7FFFFFFF && (lane == 0 || key[r] != prev);
+    bal[r] = __builtin_amdgcn_ballot_w64(keep);
+    tb[r] = __builtin_amdgcn_ballot_w64(keep && (int64_t)key[r] == tg[r] - a.offset);
+    x[r] = 0.f;
+    if (keep) {
+      const int64_t o = (row0 + r) * a.lstride + key[r];
+      x[r] = a.bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.logits)[o])
+                    : reinterpret_cast<const float*>(a.logits)[o];
     }
   }
-  const int prev = __shfl_up(key, 1);
-  const bool keep = key != 0x7FFFFFFF && (lane == 0 || key != prev);
-  const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
-  const int n = __popcll(bal);
-  const int p = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-  const int64_t tg = a.targets[row];
-  if (tg < 0 || tg >= a.real_vocab) status |= LLP_STATUS_TARGET_OUT_OF_RANGE;
-  const int64_t tloc = tg - a.offset;
-  float x = 0.f;
-  if (keep) {
-    const int64_t o = row * a.lstride + key;
-    x = a.bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.logits)[o])
-               : reinterpret_cast<const float*>(a.logits)[o];
-    zs[w][p] = x * a.c1;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int p = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[r] >> 32),
+                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal[r], 0));
+    if ((bal[r] >> lane) & 1) zs[w][r][p] = x[r] * a.c1;
   }
-  const bool has_t = keep && (int64_t)key == tloc;
-  const uint64_t tb = __builtin_amdgcn_ballot_w64(has_t);
-  // zs[w] is private to this wave; one wave's LDS accesses complete in issue order.
   __builtin_amdgcn_wave_barrier();
-  float M;
-  const float e = wave_set_sum(lane < n ? zs[w][lane] : -INFINITY, lane < n, M);
-  if (lane == 0) {
-    if (n == 0) {
-      a.out_t[row] = 0.f;
-      a.out_f[row] = 0;
-      a.out_l[row] = -INFINITY;
-      if (a.out_p) a.out_p[row] = -INFINITY;
-    } else {
-      const float lse = M + logf(e);
-      float t = 0.f;
-      // The target's compact position = kept lanes below the (single) lane holding it.
-      if (tb) t = zs[w][__popcll(bal & ((tb & (0 - tb)) - 1))];
-      a.out_t[row] = tb ? t : 0.f;
-      a.out_f[row] = tb ? 1 : 0;
-      a.out_l[row] = lse;
-      if (a.out_p) a.out_p[row] = tb ? t - lse : -INFINITY;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    if (r >= nr) break;
+    const int64_t row = row0 + r;
+    if (!scored[r]) {
+      if (lane == 0) {
+        a.out_t[row] = 0.f;
+        a.out_f[row] = 0;
+        a.out_l[row] = 0.f;
+        if (a.out_p) a.out_p[row] = 0.f;
+      }
+      continue;
+    }
+    if (tg[r] < 0 || tg[r] >= a.real_vocab) status |= LLP_STATUS_TARGET_OUT_OF_RANGE;
+    const int n = __popcll(bal[r]);
+    float M;
+    const float e = wave_set_sum(lane < n ? zs[w][r][lane] : -INFINITY, lane < n, M, pow2_ceil(n));
+    if (lane == 0) {
+      if (n == 0) {
+        a.out_t[row] = 0.f;
+        a.out_f[row] = 0;
+        a.out_l[row] = -INFINITY;
+        if (a.out_p) a.out_p[row] = -INFINITY;
+      } else {
+        const float lse = M + logf(e);
+        float t = 0.f;
+        // The target's compact position = kept lanes below the (single) lane holding it.
+        if (tb[r]) t = zs[w][r][__popcll(bal[r] & ((tb[r] & (0 - tb[r])) - 1))];
+        a.out_t[row] = tb[r] ? t : 0.f;
+        a.out_f[row] = tb[r] ? 1 : 0;
+        a.out_l[row] = lse;
+        if (a.out_p) a.out_p[row] = tb[r] ? t - lse : -INFINITY;
+      }
     }
   }
   if (a.status) {
@@ -1115,7 +1165,7 @@ __global__ __launch_bounds__(256) void k_keep(KeepArgs a) {
     const bool live = lane < total;
     const float z = live ? load1(xr, a.bf16, list[w][lane]) * a.c1 : -INFINITY;
     float M;
-    const float e = wave_set_sum(z, live, M);
+    const float e = wave_set_sum(z, live, M, pow2_ceil(total));
     lse = M + logf(e);
   } else if (total > 64) {
     float M = lm, S = ls;
@@ -1173,7 +1223,11 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_topp(const ToppArgs& a, hipStream_t s) {
-  if (a.T > 0) hipLaunchKernelGGL(k_topp, dim3(ceil_div64(a.T, 4)), dim3(256), 0, s, a);
+  // One row per wave while the rows fit the chip's wave slots about twice (most memory-level
+  // parallelism); past that, 4 rows per wave overlap the rows' memory latencies. The rows
+  // per wave do not change any row's result.
+  if (a.T >= 32768) hipLaunchKernelGGL(k_topp<4>, dim3(ceil_div64(a.T, 16)), dim3(256), 0, s, a);
+  else if (a.T > 0) hipLaunchKernelGGL(k_topp<1>, dim3(ceil_div64(a.T, 4)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -243,3 +243,42 @@ def test_config5_logits_forward_and_keep_mask_full(llp):
         for k in ("target_logit", "in_range", "lse", "logp"):
             assert torch.equal(a[k], b[k]), (r, k)
     say("config5 full: dense keep mask == compact scorer bitwise on 4 shards")
+
+
+def test_topp_rows_per_wave_paths_bitwise(llp):
+    """From T = 32768 rows a wave scores 4 rows at a time. With a ragged T (a last wave of
+    fewer rows) every row gets the bits the one-row-per-wave path gives it (the same rows in
+    calls of 16384) and the bits of the dense keep-mask scorer; sampled rows match the
+    oracle. Masked rows, empty rows and an invalid id are included, over a full-vocabulary
+    call and a shard."""
+    x, ids, tg = topp_small()
+    T = 32768 + 13
+    idx = np.arange(T) % x.shape[0]
+    X, I, G = dev(x[idx]), ids[idx].copy(), tg[idx]
+    I[7, 2] = 640                          # padded id: invalid, ignored
+    I[11] = -1                             # empty row
+    km = dense_mask(np.where(I >= 600, -1, I), 640)
+    mask = (synth.rng(93, 1).random(T) > 0.1).astype(np.uint8)
+    Id, Gd, Md, Kd = dev(I), dev(G), dev(mask), dev(km)
+    for lo, hi in ((0, 640), (160, 320)):
+        say(f"topp rows-per-wave paths, columns [{lo}, {hi})")
+        kw = dict(temperature=0.7, offset=lo, real_vocab=600, padded_vocab=640,
+                  world=1 if (lo, hi) == (0, 640) else 4, local_size=hi - lo)
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        big = llp.top_p_replay(X[:, lo:hi], Id, Gd, loss_mask=Md, status=st, **kw)
+        parts = [llp.top_p_replay(X[s:s + 16384, lo:hi], Id[s:s + 16384], Gd[s:s + 16384],
+                                  loss_mask=Md[s:s + 16384], **kw) for s in range(0, T, 16384)]
+        dense = llp.keep_mask_replay(X[:, lo:hi], Kd[:, lo:hi], Gd, loss_mask=Md, **kw)
+        torch.cuda.synchronize()
+        assert int(st.item()) & llp.STATUS_BITS["REPLAY_ID_INVALID"]
+        for k in ("target_logit", "in_range", "lse", "logp"):
+            one = torch.cat([p[k] for p in parts])
+            assert torch.equal(big[k], one), (lo, hi, k)
+            assert torch.equal(big[k], dense[k]), (lo, hi, k)
+        rows = np.unique(np.concatenate([np.arange(16), np.arange(T - 29, T),
+                                         synth.rng(93, 2).integers(0, T, 200)]))
+        ref = oracle.top_p_replay(x[idx[rows]][:, lo:hi], I[rows], G[rows], 0.7, lo, hi - lo,
+                                  600, mask[rows])
+        for k in ("lse", "logp"):
+            assert_rows_close(host(big[k])[rows], ref[k], LOGP_ATOL, f"topp {k} [{lo},{hi})")
+        np.testing.assert_array_equal(host(big["in_range"])[rows], ref["in_range"])
