@@ -455,118 +455,164 @@ __device__ __forceinline__ int pow2_ceil(int n) {
   return p;
 }
 
-// A wave scores RPW consecutive rows: every row's loads (ids, target, mask) are issued first,
-// and later every row's logit gathers, so a wave waits two memory latencies per RPW rows;
-// each row's arithmetic is the one-row arithmetic.
-template <int RPW>
-__global__ __launch_bounds__(256) void k_topp(ToppArgs a) {
-  __shared__ float zs[4][RPW][64];
-  __shared__ int ks[4][RPW][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + w) * RPW;
-  if (row0 >= a.T) return;
-  const int nr = a.T - row0 < RPW ? (int)(a.T - row0) : RPW;
-  int status = 0;
-  // A row past T repeats the last row: read, never written.
-  int64_t id[RPW], tg[RPW];
-  bool scored[RPW];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int64_t row = row0 + (r < nr ? r : nr - 1);
-    id[r] = lane < a.K ? a.ids[row * a.ids_stride + lane] : -1;
-    tg[r] = a.targets[row];
-    scored[r] = r < nr && (a.mask == nullptr || a.mask[row] != 0);
+constexpr int TOPP_SENT = 0x7FFFFFFF;  // sorts after every local key
+
+// One scored row by the whole wave: lane k holds slot k. The path of rows whose shard holds more
+// than 16 of the row's listed ids; its bits are those of the grouped path below for any row
+// both can score. zsw / ksw: this wave's 64-entry LDS scratch (private to the wave; one
+// wave's LDS accesses complete in issue order).
+__device__ __forceinline__ void topp_row64(const ToppArgs& a, int64_t row, int lane, float* zsw,
+                                           int* ksw) {
+  int64_t id = lane < a.K ? a.ids[row * a.ids_stride + lane] : -1;
+  if (id < -1 || id >= a.real_vocab) id = -1;   // its status bit is set by the grouped pass
+  const int64_t loc = id - a.offset;
+  const bool in_shard = id >= 0 && loc >= 0 && loc < a.n_real;
+  const uint64_t vb = __builtin_amdgcn_ballot_w64(in_shard);
+  const int c = __popcll(vb);
+  if (in_shard)
+    ksw[__builtin_amdgcn_mbcnt_hi((uint32_t)(vb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)vb, 0))] =
+        (int)loc;
+  __builtin_amdgcn_wave_barrier();
+  int key = lane < c ? ksw[lane] : TOPP_SENT;
+  const int P = pow2_ceil(c);
+  for (int k = 2; k <= P; k <<= 1)
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      const int other = __shfl_xor(key, jj);
+      const bool up = (lane & k) == 0, lower = (lane & jj) == 0;
+      key = (lower == up) ? min(key, other) : max(key, other);
+    }
+  const int prev = __shfl_up(key, 1);
+  const bool keep = key != TOPP_SENT && (lane == 0 || key != prev);
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+  const int n = __popcll(bal);
+  const int64_t tg = a.targets[row];
+  const uint64_t tb = __builtin_amdgcn_ballot_w64(keep && (int64_t)key == tg - a.offset);
+  if (keep) {
+    const int64_t o = row * a.lstride + key;
+    const float x = a.bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.logits)[o])
+                           : reinterpret_cast<const float*>(a.logits)[o];
+    zsw[__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0))] =
+        x * a.c1;
   }
-  int key[RPW];
+  __builtin_amdgcn_wave_barrier();
+  float M;
+  const float e = wave_set_sum(lane < n ? zsw[lane] : -INFINITY, lane < n, M, pow2_ceil(n));
+  if (lane == 0) {
+    const float lse = M + logf(e);   // n >= 1: the shard holds more than 16 listed ids
+    const float t = tb ? zsw[__popcll(bal & ((tb & (0 - tb)) - 1))] : 0.f;
+    a.out_t[row] = t;
+    a.out_f[row] = tb ? 1 : 0;
+    a.out_l[row] = lse;
+    if (a.out_p) a.out_p[row] = tb ? t - lse : -INFINITY;
+  }
+}
+
+// A wave scores 4 consecutive rows at once, 16 lanes per row (group g = lane / 16 takes row
+// row0 + g, lane l of the group slots l, l + 16, l + 32, l + 48). A group packs its row's
+// in-shard keys into its lanes (at most 16; a row with more goes to topp_row64 afterwards),
+// sorts them with the bitonic network over the wave-wide largest power of two P <= 16 that
+// any group needs (partners l ^ jj, jj < P, stay in the group; extra stages leave a sorted
+// group unchanged), dedups, compacts, gathers and sums with wave_set_sum, whose steps off < 16
+// stay in the group: lane 16g pairs with the group's lanes exactly as lane 0 pairs with lanes
+// 0..15 in the whole-wave form, and every other partner adds a zero (or -inf to the max), so
+// each row gets the bits of the whole-wave path.
+__global__ __launch_bounds__(256) void k_topp(ToppArgs a) {
+  __shared__ float zs[4][64];
+  __shared__ int ks[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, gl = lane & 15;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + w) * 4;
+  if (row0 >= a.T) return;
+  const int64_t row = row0 + g;
+  const bool in_rows = row < a.T;
+  const int64_t rr = in_rows ? row : a.T - 1;   // a group past T reads the last row, writes nothing
+  const bool scored = in_rows && (a.mask == nullptr || a.mask[rr] != 0);
+  const int64_t tg = a.targets[rr];
+  int status = 0;
+  int64_t id[4];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    int64_t v = id[r];
+  for (int j = 0; j < 4; ++j) {
+    const int sl = gl + 16 * j;
+    id[j] = sl < a.K ? a.ids[rr * a.ids_stride + sl] : -1;
+  }
+  const uint64_t gm = 0xFFFFull << (16 * g);
+  const uint64_t lower = (1ull << lane) - 1;
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int64_t v = id[j];
     if (v < -1 || v >= a.real_vocab) {
-      if (r < nr) status |= LLP_STATUS_REPLAY_ID_INVALID;
+      if (in_rows) status |= LLP_STATUS_REPLAY_ID_INVALID;
       v = -1;
     }
     const int64_t loc = v - a.offset;
-    const bool in_shard = scored[r] && v >= 0 && loc >= 0 && loc < a.n_real;
-    // Pack the in-shard keys into lanes 0..c-1 (ks[w] is private to this wave; one wave's
-    // LDS accesses complete in issue order).
-    const uint64_t vb = __builtin_amdgcn_ballot_w64(in_shard);
-    const int c = __popcll(vb);
-    if (in_shard)
-      ks[w][r][__builtin_amdgcn_mbcnt_hi((uint32_t)(vb >> 32),
-                                         __builtin_amdgcn_mbcnt_lo((uint32_t)vb, 0))] = (int)loc;
-    __builtin_amdgcn_wave_barrier();
-    int k0 = lane < c ? ks[w][r][lane] : 0x7FFFFFFF;
-    // Bitonic sort of lanes 0..P-1, ascending; the partners of lane l (l ^ jj, jj < P) stay in
-    // its block of P lanes, which past lane c holds sentinels only.
-    const int P = pow2_ceil(c);
-    for (int k = 2; k <= P; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        const int other = __shfl_xor(k0, jj);
-        const bool up = (lane & k) == 0;
-        const bool lower = (lane & jj) == 0;
-        const int lo = min(k0, other), hi = max(k0, other);
-        k0 = (lower == up) ? lo : hi;
-      }
-    }
-    key[r] = k0;
+    const bool ins = scored && v >= 0 && loc >= 0 && loc < a.n_real;
+    const uint64_t bj = __builtin_amdgcn_ballot_w64(ins) & gm;
+    const int pos = c + __popcll(bj & lower);
+    if (ins && pos < 16) ks[w][16 * g + pos] = (int)loc;
+    c += __popcll(bj);
   }
-  // Dedup and compaction; the gathers of every row's distinct logits go out together.
-  uint64_t bal[RPW], tb[RPW];
-  float x[RPW];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int prev = __shfl_up(key[r], 1);
-    const bool keep = key[r] != 0x7FFFFFFF && (lane == 0 || key[r] != prev);
-    bal[r] = __builtin_amdgcn_ballot_w64(keep);
-    tb[r] = __builtin_amdgcn_ballot_w64(keep && (int64_t)key[r] == tg[r] - a.offset);
-    x[r] = 0.f;
-    if (keep) {
-      const int64_t o = (row0 + r) * a.lstride + key[r];
-      x[r] = a.bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.logits)[o])
-                    : reinterpret_cast<const float*>(a.logits)[o];
+  const bool wide = c > 16;
+  __builtin_amdgcn_wave_barrier();
+  int key = (!wide && gl < c) ? ks[w][16 * g + gl] : TOPP_SENT;
+  int P = pow2_ceil(wide ? 1 : c);
+  P = max(P, __shfl_xor(P, 16));
+  P = max(P, __shfl_xor(P, 32));
+  P = __builtin_amdgcn_readfirstlane(P);
+  for (int k = 2; k <= P; k <<= 1)
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      // Direction from the lane's index in its group: at k = 16 every group sorts ascending.
+      const int other = __shfl_xor(key, jj);
+      const bool up = (gl & k) == 0, lo = (gl & jj) == 0;
+      key = (lo == up) ? min(key, other) : max(key, other);
     }
-  }
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int p = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[r] >> 32),
-                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal[r], 0));
-    if ((bal[r] >> lane) & 1) zs[w][r][p] = x[r] * a.c1;
+  const int prev = __shfl_up(key, 1);
+  const bool keep = key != TOPP_SENT && (gl == 0 || key != prev);
+  const uint32_t gb = (uint32_t)((__builtin_amdgcn_ballot_w64(keep) & gm) >> (16 * g));
+  const uint32_t tbg =
+      (uint32_t)((__builtin_amdgcn_ballot_w64(keep && (int64_t)key == tg - a.offset) & gm) >> (16 * g));
+  const int n = __popc(gb);
+  if (keep) {
+    const int64_t o = row * a.lstride + key;
+    const float x = a.bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.logits)[o])
+                           : reinterpret_cast<const float*>(a.logits)[o];
+    zs[w][16 * g + __popc(gb & ((1u << gl) - 1))] = x * a.c1;
   }
   __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    if (r >= nr) break;
-    const int64_t row = row0 + r;
-    if (!scored[r]) {
-      if (lane == 0) {
-        a.out_t[row] = 0.f;
-        a.out_f[row] = 0;
-        a.out_l[row] = 0.f;
-        if (a.out_p) a.out_p[row] = 0.f;
-      }
-      continue;
+  int span = pow2_ceil(n);
+  span = max(span, __shfl_xor(span, 16));
+  span = max(span, __shfl_xor(span, 32));
+  span = __builtin_amdgcn_readfirstlane(span);
+  float M;
+  const float e = wave_set_sum(gl < n ? zs[w][16 * g + gl] : -INFINITY, gl < n, M, span);
+  if (scored && (tg < 0 || tg >= a.real_vocab)) status |= LLP_STATUS_TARGET_OUT_OF_RANGE;
+  if (gl == 0 && in_rows && !wide) {
+    if (!scored) {
+      a.out_t[row] = 0.f;
+      a.out_f[row] = 0;
+      a.out_l[row] = 0.f;
+      if (a.out_p) a.out_p[row] = 0.f;
+    } else if (n == 0) {
+      a.out_t[row] = 0.f;
+      a.out_f[row] = 0;
+      a.out_l[row] = -INFINITY;
+      if (a.out_p) a.out_p[row] = -INFINITY;
+    } else {
+      const float lse = M + logf(e);
+      // The target's compact position = kept lanes of the group below the one holding it.
+      const float t = tbg ? zs[w][16 * g + __popc(gb & ((tbg & (0u - tbg)) - 1))] : 0.f;
+      a.out_t[row] = t;
+      a.out_f[row] = tbg ? 1 : 0;
+      a.out_l[row] = lse;
+      if (a.out_p) a.out_p[row] = tbg ? t - lse : -INFINITY;
     }
-    if (tg[r] < 0 || tg[r] >= a.real_vocab) status |= LLP_STATUS_TARGET_OUT_OF_RANGE;
-    const int n = __popcll(bal[r]);
-    float M;
-    const float e = wave_set_sum(lane < n ? zs[w][r][lane] : -INFINITY, lane < n, M, pow2_ceil(n));
-    if (lane == 0) {
-      if (n == 0) {
-        a.out_t[row] = 0.f;
-        a.out_f[row] = 0;
-        a.out_l[row] = -INFINITY;
-        if (a.out_p) a.out_p[row] = -INFINITY;
-      } else {
-        const float lse = M + logf(e);
-        float t = 0.f;
-        // The target's compact position = kept lanes below the (single) lane holding it.
-        if (tb[r]) t = zs[w][r][__popcll(bal[r] & ((tb[r] & (0 - tb[r])) - 1))];
-        a.out_t[row] = tb[r] ? t : 0.f;
-        a.out_f[row] = tb[r] ? 1 : 0;
-        a.out_l[row] = lse;
-        if (a.out_p) a.out_p[row] = tb[r] ? t - lse : -INFINITY;
-      }
-    }
+  }
+  // Rows whose shard holds more than 16 of their ids: the whole wave, one row at a time.
+  uint64_t wb = __builtin_amdgcn_ballot_w64(wide && gl == 0);
+  while (wb) {
+    const int gg = __builtin_ctzll(wb) >> 4;
+    wb &= wb - 1;
+    topp_row64(a, row0 + gg, lane, zs[w], ks[w]);
   }
   if (a.status) {
     const uint64_t any = __builtin_amdgcn_ballot_w64(status != 0);
@@ -1223,11 +1269,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_topp(const ToppArgs& a, hipStream_t s) {
-  // One row per wave while the rows fit the chip's wave slots about twice (most memory-level
-  // parallelism); past that, 4 rows per wave overlap the rows' memory latencies. The rows
-  // per wave do not change any row's result.
-  if (a.T >= 32768) hipLaunchKernelGGL(k_topp<4>, dim3(ceil_div64(a.T, 16)), dim3(256), 0, s, a);
-  else if (a.T > 0) hipLaunchKernelGGL(k_topp<1>, dim3(ceil_div64(a.T, 4)), dim3(256), 0, s, a);
+  if (a.T > 0) hipLaunchKernelGGL(k_topp, dim3(ceil_div64(a.T, 16)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

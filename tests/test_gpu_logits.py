@@ -245,12 +245,14 @@ def test_config5_logits_forward_and_keep_mask_full(llp):
     say("config5 full: dense keep mask == compact scorer bitwise on 4 shards")
 
 
-def test_topp_rows_per_wave_paths_bitwise(llp):
-    """From T = 32768 rows a wave scores 4 rows at a time. With a ragged T (a last wave of
-    fewer rows) every row gets the bits the one-row-per-wave path gives it (the same rows in
-    calls of 16384) and the bits of the dense keep-mask scorer; sampled rows match the
-    oracle. Masked rows, empty rows and an invalid id are included, over a full-vocabulary
-    call and a shard."""
+def test_topp_row_position_invariance_bitwise(llp):
+    """A wave scores 4 rows at once, 16 lanes each, and falls back to the whole wave for a
+    row whose shard holds more than 16 of its ids. Every row gets the same bits wherever it
+    lands: the same rows scored in calls that start at other rows (so each row sits in another
+    lane group and wave), with a ragged T, equal the dense keep-mask scorer bit for bit, and
+    sampled rows match the oracle. Rows of up to 40 distinct ids (the full-vocabulary call
+    takes the fallback), masked rows, empty rows and an invalid id are included, over a
+    full-vocabulary call and a shard."""
     x, ids, tg = topp_small()
     T = 32768 + 13
     idx = np.arange(T) % x.shape[0]
@@ -266,8 +268,9 @@ def test_topp_rows_per_wave_paths_bitwise(llp):
                   world=1 if (lo, hi) == (0, 640) else 4, local_size=hi - lo)
         st = torch.zeros(1, dtype=torch.int32, device="cuda")
         big = llp.top_p_replay(X[:, lo:hi], Id, Gd, loss_mask=Md, status=st, **kw)
-        parts = [llp.top_p_replay(X[s:s + 16384, lo:hi], Id[s:s + 16384], Gd[s:s + 16384],
-                                  loss_mask=Md[s:s + 16384], **kw) for s in range(0, T, 16384)]
+        cuts = [0, 5, 16387, 16390, T]
+        parts = [llp.top_p_replay(X[s:e, lo:hi], Id[s:e], Gd[s:e], loss_mask=Md[s:e], **kw)
+                 for s, e in zip(cuts[:-1], cuts[1:])]
         dense = llp.keep_mask_replay(X[:, lo:hi], Kd[:, lo:hi], Gd, loss_mask=Md, **kw)
         torch.cuda.synchronize()
         assert int(st.item()) & llp.STATUS_BITS["REPLAY_ID_INVALID"]
