@@ -330,7 +330,7 @@ LLP_API llp_status llp_open(int32_t device, llp_info* info) {
     snprintf(info->version, sizeof(info->version), "%s", LLP_VERSION);
     snprintf(info->arch, sizeof(info->arch), "%.31s", prop.gcnArchName);
     snprintf(info->route, sizeof(info->route),
-             "hip-gfx950 mfma32x32x16bf16 tile256x256 bk64 lds-dma-2stage w4 xcd8 vgroup8 dhsplit%d",
+             "hip-gfx950 mfma32x32x16bf16 tile256x256 bk64 lds-dma-2stage fwd-w8 bwd-w4 xcd8 vgroup8 dhsplit%d",
              DH_SPLITS);
     info->max_replay_ids = LLP_MAX_REPLAY_IDS;
     info->num_cus = prop.multiProcessorCount;

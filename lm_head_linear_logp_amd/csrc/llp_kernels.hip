@@ -131,8 +131,8 @@ __device__ __forceinline__ void bias16(const void* bias, int vb, int lane, int64
 
 // Starting accumulators of a vocabulary x token tile at v0: each lane's rows get their bias (the
 // same for all its token blocks).
-template <bool F32>
-__device__ __forceinline__ void bias_acc(f32x16 (&acc)[4][4], const void* bias, int v0,
+template <bool F32, int NFB>
+__device__ __forceinline__ void bias_acc(f32x16 (&acc)[4][NFB], const void* bias, int v0,
                                          int64_t n_real) {
   const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) & 1;
 #pragma unroll
@@ -140,7 +140,7 @@ __device__ __forceinline__ void bias_acc(f32x16 (&acc)[4][4], const void* bias, 
     float b[16];
     bias16<F32>(bias, v0 + wm * 128 + mi * 32, lane, n_real, b);
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < NFB; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = b[r];
   }
@@ -150,29 +150,33 @@ __device__ __forceinline__ void bias_acc(f32x16 (&acc)[4][4], const void* bias, 
 __device__ __forceinline__ void init_acc(f32x16 (&acc)[4][4], const void* bias, bool bias_f32,
                                          int v0, int64_t n_real) {
   if (bias == nullptr) zero_acc(acc);
-  else if (bias_f32) bias_acc<true>(acc, bias, v0, n_real);
-  else bias_acc<false>(acc, bias, v0, n_real);
+  else if (bias_f32) bias_acc<true, 4>(acc, bias, v0, n_real);
+  else bias_acc<false, 4>(acc, bias, v0, n_real);
 }
 
 constexpr int BIAS_NONE = 0, BIAS_BF16 = 1, BIAS_F32 = 2;
 
-template <bool TAIL>
-__device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const FwdArgs& a, int vt,
+// NFB = 4: 4 waves (2 x 2) of 128 vocabulary columns x 128 tokens; NFB = 2: 8 waves (2 x 4)
+// of 128 x 64. Either way a token's values are reduced in the same order: down the lane's
+// 64 values of its wave's 128 columns (mi, r), the lane pair, then the two column halves.
+template <bool TAIL, int NFB>
+__device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][NFB], const FwdArgs& a, int vt,
                                              int v0, int j0, int Ts, uint16_t* smem) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
+  constexpr int TW = 32 * NFB;  // tokens per wave
   const int vbase = v0 + wm * 128;
   float* red = reinterpret_cast<float*>(smem);  // [6][256]: max0 max1 s0 s1 q0 q1
   // Pass 1: per-token max of x over this lane's 64 columns, the lane pair (l, l^32) and the two
   // waves holding the tile's two column halves. z = x * c1 with c1 > 0 and rounding is
   // monotonic, so fl(max x * c1) is the max of z.
-  float mx[4];
+  float mx[NFB];
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) mx[ni] = -INFINITY;
+  for (int ni = 0; ni < NFB; ++ni) mx[ni] = -INFINITY;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < NFB; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float x = acc[mi][ni][r];
@@ -181,25 +185,27 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const Fw
       }
   }
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
+  for (int ni = 0; ni < NFB; ++ni) {
     mx[ni] = fmaxf(mx[ni], __shfl_xor(mx[ni], 32));
-    if (lane < 32) red[wm * 256 + wn * 128 + ni * 32 + lane] = mx[ni];
+    if (lane < 32) red[wm * 256 + wn * TW + ni * 32 + lane] = mx[ni];
   }
   __syncthreads();
   // Pass 2: s = sum 2^d2, q = sum 2^d2 * d2 with d2 = (z - M) log2(e) = x c1 log2(e) - M log2(e).
   const float c1l = a.c1 * kLog2e;
-  float ml[4];
+  float ml[NFB];
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int tn = wn * 128 + ni * 32 + (lane & 31);
+  for (int ni = 0; ni < NFB; ++ni) {
+    const int tn = wn * TW + ni * 32 + (lane & 31);
     mx[ni] = fmaxf(red[tn], red[256 + tn]) * a.c1;
     ml[ni] = mx[ni] * kLog2e;
   }
-  float sv[4] = {0.f, 0.f, 0.f, 0.f}, qv[4] = {0.f, 0.f, 0.f, 0.f};
+  float sv[NFB], qv[NFB];
+#pragma unroll
+  for (int ni = 0; ni < NFB; ++ni) sv[ni] = qv[ni] = 0.f;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < NFB; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float d2 = fmaf(acc[mi][ni][r], c1l, -ml[ni]);
@@ -211,20 +217,20 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const Fw
       }
   }
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
+  for (int ni = 0; ni < NFB; ++ni) {
     // (x + y) == (y + x): both lanes of a pair hold the same sum.
     sv[ni] += __shfl_xor(sv[ni], 32);
     qv[ni] += __shfl_xor(qv[ni], 32);
     if (lane < 32) {
-      const int tn = wn * 128 + ni * 32 + lane;
+      const int tn = wn * TW + ni * 32 + lane;
       red[512 + wm * 256 + tn] = sv[ni];
       red[1024 + wm * 256 + tn] = qv[ni];
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int tn = wn * 128 + ni * 32 + (lane & 31);
+  for (int ni = 0; ni < NFB; ++ni) {
+    const int tn = wn * TW + ni * 32 + (lane & 31);
     const int j = j0 + tn;
     if (wm == 0 && lane < 32 && j < Ts) {
       const int64_t o = (int64_t)vt * a.pstride + j;
@@ -253,18 +259,19 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][4], const Fw
 // rows j0 .. (clamped below the count), gathered through `scored` (ascending). The hidden
 // resource starts at the tile's first scored row; the host keeps T * hidden_stride * 2 below
 // 2^31 bytes, so every lane offset fits in 32 bits.
+template <int NW>
 __device__ __forceinline__ void weight_hidden_loaders(const uint16_t* W, int64_t ldw, int64_t n_real,
                                                       int v0, const uint16_t* h, int64_t ldh,
                                                       const int32_t* scored, int j0, int Ts, int H,
-                                                      dma::Loader& la, dma::Loader& lb) {
+                                                      dma::LoaderT<NW>& la, dma::LoaderT<NW>& lb) {
   const int nv = n_real - v0 < BM ? (int)(n_real - v0) : BM;
   const int nj = Ts - j0 < BN ? Ts - j0 : BN;
   const int64_t h0 = scored[j0];
   la.init(W + (int64_t)v0 * ldw, (uint64_t)((nv - 1) * ldw + H) * 2);
   lb.init(h + h0 * ldh, (uint64_t)((scored[j0 + nj - 1] - h0) * ldh + H) * 2);
 #pragma unroll
-  for (int u = 0; u < dma::NI; ++u) {
-    const int r = dma::Loader::row_of(u);
+  for (int u = 0; u < dma::LoaderT<NW>::NIW; ++u) {
+    const int r = dma::LoaderT<NW>::row_of(u);
     la.set(u, r < nv ? r : nv - 1, ldw);
     lb.set(u, scored[j0 + (r < nj ? r : nj - 1)] - h0, ldh);
   }
@@ -276,24 +283,31 @@ static_assert(dma::BKD == KSTEP, "K step shared with the host");
 
 // One kernel per bias mode, differing only in how the accumulators start: a run-time choice
 // there makes the compiler spill accumulators in the epilogue.
-template <int BMODE>
-__global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_fwd(FwdArgs a) {
+// The forward tile runs FWD_WAVES = 8 waves, two per SIMD: each wave holds 128 x 64 outputs (128
+// accumulators), so one wave's LDS reads, DMA issue and barrier waits overlap the other's
+// MFMAs. Every output's MFMA chain and every token's reduction order are those of the 4-wave
+// tile (1 wave per SIMD, 128 x 128 per wave).
+constexpr int FWD_WAVES = 8;
+
+template <int BMODE, int NW>
+__global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_fwd(FwdArgs a) {
+  constexpr int NFB = 16 / NW;
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
   int vt, tb;
   vocab_token_tile(xcd_remap(blockIdx.x, gridDim.x), a.nvt, a.ntb, vt, tb);
   const int Ts = *a.count;
   const int j0 = tb * BN, v0 = vt * BM;
   if (j0 >= Ts) return;
-  dma::Loader la, lb;
-  weight_hidden_loaders(a.W, a.ldw, a.n_real, v0, a.h, a.ldh, a.scored, j0, Ts, a.H, la, lb);
-  f32x16 acc[4][4];
+  dma::LoaderT<NW> la, lb;
+  weight_hidden_loaders<NW>(a.W, a.ldw, a.n_real, v0, a.h, a.ldh, a.scored, j0, Ts, a.H, la, lb);
+  f32x16 acc[4][NFB];
   if constexpr (BMODE == BIAS_NONE) zero_acc(acc);
-  else bias_acc<BMODE == BIAS_F32>(acc, a.bias, v0, a.n_real);
+  else bias_acc<BMODE == BIAS_F32, NFB>(acc, a.bias, v0, a.n_real);
   dma::mainloop(la, lb, 0, a.H / dma::BKD, smem, acc);
   if (v0 + BM > a.n_real)
-    fwd_epilogue<true>(acc, a, vt, v0, j0, Ts, smem);
+    fwd_epilogue<true, NFB>(acc, a, vt, v0, j0, Ts, smem);
   else
-    fwd_epilogue<false>(acc, a, vt, v0, j0, Ts, smem);
+    fwd_epilogue<false, NFB>(acc, a, vt, v0, j0, Ts, smem);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1248,10 +1262,10 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   if (a.nvt > 0 && a.ntb > 0) {
-    const dim3 grid(a.nvt * a.ntb), block(NTHREADS);
-    if (a.bias == nullptr) hipLaunchKernelGGL(k_fwd<BIAS_NONE>, grid, block, 0, s, a);
-    else if (a.bias_f32) hipLaunchKernelGGL(k_fwd<BIAS_F32>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(k_fwd<BIAS_BF16>, grid, block, 0, s, a);
+    const dim3 grid(a.nvt * a.ntb), block(64 * FWD_WAVES);
+    if (a.bias == nullptr) hipLaunchKernelGGL((k_fwd<BIAS_NONE, FWD_WAVES>), grid, block, 0, s, a);
+    else if (a.bias_f32) hipLaunchKernelGGL((k_fwd<BIAS_F32, FWD_WAVES>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_fwd<BIAS_BF16, FWD_WAVES>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -1333,7 +1347,7 @@ hipError_t launch_keep(const KeepArgs& a, hipStream_t s) {
 
 hipError_t probe_kernels() {
   hipFuncAttributes attr;
-  return hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(k_fwd<BIAS_NONE>));
+  return hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(k_fwd<BIAS_NONE, FWD_WAVES>));
 }
 
 }  // namespace llp

@@ -1,11 +1,13 @@
 // llp_tile.hpp -- the bf16 MFMA GEMM tile for gfx950 shared by the fused forward, the
 // gradient recompute and the two backward products.
 //
-// Workgroup tile: BM x BN = 256 x 256 outputs, 256 threads = 4 wave64s in a 2 x 2 arrangement,
-// each wave owning a 128 x 128 sub-tile as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32
-// accumulators per lane, held in AGPRs). Both operands are K-contiguous in memory ([rows][K]
-// with K innermost) and are moved into LDS by direct global->LDS loads (dma:: below); every
-// kernel that needs a transposed operand gets a K-contiguous copy first.
+// Workgroup tile: BM x BN = 256 x 256 outputs. With 4 wave64s (2 x 2, one per SIMD) each wave
+// owns a 128 x 128 sub-tile as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators
+// per lane, held in AGPRs); with 8 wave64s (2 x 4, two per SIMD, the forward) each owns
+// 128 x 64 as 4 x 2 blocks (128 accumulators), NFB = 2 fragments of B. The stages, the DMA
+// pattern and every output's MFMA chain are the same either way. Operands are read either
+// K-contiguous ([rows][K], K innermost) or K-major, through direct global->LDS loads (dma::
+// below).
 //
 // MFMA 32x32x16 bf16 lane layout (CDNA4 ISA): lane l supplies A[i][k] and B[k][j] for
 // i, j = l % 32 and k = 8 * (l / 32) + 0..7; accumulator register r of lane l holds D[i][j]
@@ -77,11 +79,12 @@ __device__ __forceinline__ float acc_read(float x) {
   return r;
 }
 
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+template <int NFB>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][NFB]) {
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < NFB; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 }
@@ -109,40 +112,51 @@ __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
 // One operand's loads: a buffer resource whose base is the operand's first row in the tile, and
 // per load instruction this lane's 32-bit byte offset at K step 0; the K step's offset goes in
 // the instruction's scalar offset. Offsets are exact (rows clamped by the caller), so every
-// access lies inside [base, base + bytes), the range given to the resource.
-struct Loader {
+// access lies inside [base, base + bytes), the range given to the resource. With NW waves a
+// wave fills 256 / NW rows of each operand with NIW = 32 / NW instructions.
+// The buffer resource and the DMA instruction, outside the loader template (non-template
+// functions, like the rest of the device code, are parsed once; the host pass rejects these
+// builtins inside a class template's instantiation).
+struct BufRsrc {
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t voff[NI];
-
-  __device__ __forceinline__ static int row_of(int u) {
-    return 64 * (threadIdx.x >> 6) + 8 * u + ((threadIdx.x & 63) >> 3);
-  }
-  __device__ __forceinline__ static int chunk_of(int u) {
-    return (threadIdx.x & 7) ^ swz8(row_of(u));
-  }
   // Raw buffer (stride 0) over `bytes` bytes from `base` (gfx9 resource word 3: 32-bit data).
   __device__ __forceinline__ void init(const uint16_t* base, uint64_t bytes) {
     rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
                                              (int)(uint32_t)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull),
                                              0x00020000);
   }
+  // 16 bytes per lane from byte offset voff + soff into the LDS window at `lds` (lane order).
+  __device__ __forceinline__ void load_lds(uint16_t* lds, uint32_t voff, int soff) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16,
+                                             voff, soff, 0, 0);
+  }
+};
+
+template <int NW>
+struct LoaderT : BufRsrc {
+  static constexpr bool KMAJOR = false;
+  static constexpr int NIW = 32 / NW;
+  static constexpr int RPW = BM / NW;  // rows per wave
+  uint32_t voff[NIW];
+
+  __device__ __forceinline__ static int row_of(int u) {
+    return RPW * (threadIdx.x >> 6) + 8 * u + ((threadIdx.x & 63) >> 3);
+  }
+  __device__ __forceinline__ static int chunk_of(int u) {
+    return (threadIdx.x & 7) ^ swz8(row_of(u));
+  }
   // Instruction u reads row `row` (relative to the base, row stride `ld` elements) for this lane.
   __device__ __forceinline__ void set(int u, int64_t row, int64_t ld) {
     voff[u] = (uint32_t)((row * ld + chunk_of(u) * 8) * 2);
   }
-  // One DMA instruction (u = 0..NI-1) of this wave for K step `kstep` into `stage`.
+  // One DMA instruction (u = 0..NIW-1) of this wave for K step `kstep` into `stage`.
   __device__ __forceinline__ void issue1(uint16_t* stage, int kstep, int u) const {
     // The wave index is uniform: keep the LDS destination (M0) in scalar registers.
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(stage + (64 * w + 8 * u) * BKD), 16,
-        voff[u], kstep * (BKD * 2), 0, 0);
-  }
-  __device__ __forceinline__ void issue(uint16_t* stage, int kstep) const {
-#pragma unroll
-    for (int u = 0; u < NI; ++u) issue1(stage, kstep, u);
+    load_lds(stage + (RPW * w + 8 * u) * BKD, voff[u], kstep * (BKD * 2));
   }
 };
+using Loader = LoaderT<4>;
 
 // A K-major operand ([K][cols] in memory, the tile's columns contiguous): a stage holds the K
 // step's 64 rows x 256 columns, 512 bytes per K-row, and 16-byte chunk c of K-row r sits at
@@ -154,6 +168,8 @@ struct Loader {
 __device__ __forceinline__ int fk(int r) { return 2 * (r & 3); }
 
 struct LoaderK {
+  static constexpr bool KMAJOR = true;
+  static constexpr int NIW = NI;
   const uint16_t* base;  // row 0, first column of the tile
   int64_t ld;            // row stride (elements)
   int maxrow;            // last readable row
@@ -194,20 +210,22 @@ struct LoaderK {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 
-template <bool KMAJ>
+template <bool KMAJ, int NF = 4>
 struct FragOp;
 
-template <>
-struct FragOp<false> {
-  int off[4], t[4];
-  __device__ __forceinline__ void init(int wx, int lane) {
+// NF fragments of 32 rows from row r0 of the stage.
+template <int NF>
+struct FragOp<false, NF> {
+  int off[NF], t[NF];
+  __device__ __forceinline__ void init_rows(int r0, int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wx * 128 + i * 32 + (lane & 31);
+    for (int i = 0; i < NF; ++i) {
+      const int r = r0 + i * 32 + (lane & 31);
       off[i] = r * BKD;
       t[i] = (lane >> 5) ^ swz8(r);
     }
   }
+  __device__ __forceinline__ void init(int wx, int lane) { init_rows(wx * 32 * NF, lane); }
   // The whole fragment (h must be 0).
   __device__ __forceinline__ bf16x8 read(const uint16_t* st, int kk, int i) const {
     return *reinterpret_cast<const bf16x8*>(st + off[i] + (((2 * kk) ^ t[i]) << 3));
@@ -215,7 +233,7 @@ struct FragOp<false> {
 };
 
 template <>
-struct FragOp<true> {
+struct FragOp<true, 4> {
   int off[4];  // bytes
   __device__ __forceinline__ void init(int wx, int lane) {
     const int g = lane >> 4, j = (lane >> 2) & 3, t = lane & 3;
@@ -240,10 +258,12 @@ struct FragOp<true> {
   }
 };
 
-template <bool AK, bool BK>
+// A wave's sub-tile: 4 fragments (128 rows) of A at wm * 128, NFB fragments of B at
+// wn * 32 * NFB.
+template <bool AK, bool BK, int NFB = 4>
 struct Frag {
   FragOp<AK> a;
-  FragOp<BK> b;
+  FragOp<BK, NFB> b;
   __device__ __forceinline__ void init(int wm, int wn, int lane) {
     a.init(wm, lane);
     b.init(wn, lane);
@@ -251,25 +271,25 @@ struct Frag {
 };
 
 // Fragments of 16-deep substep kk (0..3): lane l holds k = 16kk + 8(l/32) + 0..7.
-template <bool AK, bool BK>
+template <bool AK, bool BK, int NFB>
 __device__ __forceinline__ void load_frag(const uint16_t* As, const uint16_t* Bs,
-                                          const Frag<AK, BK>& f, int kk, bf16x8 (&a)[4],
-                                          bf16x8 (&b)[4]) {
+                                          const Frag<AK, BK, NFB>& f, int kk, bf16x8 (&a)[4],
+                                          bf16x8 (&b)[NFB]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     a[i] = f.a.read(As, kk, i);
-    b[i] = f.b.read(Bs, kk, i);
+    if (i < NFB) b[i] = f.b.read(Bs, kk, i);
   }
 }
 
 // MFMAs number lo..hi-1 of one 16-deep substep, in (mi, ni) row-major order.
-template <int LO, int HI>
-__device__ __forceinline__ void mfmas(const bf16x8 (&a)[4], const bf16x8 (&b)[4],
-                                      f32x16 (&acc)[4][4]) {
+template <int LO, int HI, int NFB>
+__device__ __forceinline__ void mfmas(const bf16x8 (&a)[4], const bf16x8 (&b)[NFB],
+                                      f32x16 (&acc)[4][NFB]) {
 #pragma unroll
   for (int k = LO; k < HI; ++k)
-    acc[k >> 2][k & 3] =
-        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k >> 2], b[k & 3], acc[k >> 2][k & 3], 0, 0, 0);
+    acc[k / NFB][k % NFB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k / NFB], b[k % NFB],
+                                                                   acc[k / NFB][k % NFB], 0, 0, 0);
 }
 
 // Wait until at most n of this wave's vector-memory instructions are outstanding
@@ -303,32 +323,38 @@ __device__ __forceinline__ void issue_range(const LA& la, const LB& lb, uint16_t
 
 // Schedule of one region: 16 MFMAs, NR fragment reads one per MFMA from the first, and D DMA
 // instructions spread evenly over the 16 MFMAs.
-template <int D, int NR, int I>
+template <int D, int NR, int I, int NM>
 __device__ __forceinline__ void region_slot() {
   __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
   if constexpr (I < NR) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-  constexpr int nv = ((I + 1) * D) / 16 - (I * D) / 16;
+  constexpr int nv = ((I + 1) * D) / NM - (I * D) / NM;
   if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, nv, 0);
-  if constexpr (I + 1 < 16) region_slot<D, NR, I + 1>();
+  if constexpr (I + 1 < NM) region_slot<D, NR, I + 1, NM>();
 }
 
 // Memory instructions of one region in slot order (the compiler keeps LDS reads and DMA
 // writes in program order, so the source order is the issue order). Reads go fragment by
 // fragment, A then B, one or two reads each (row-major or K-major); DMA instructions
 // QB + (I*D)/16 .. of step `kstep` into `dst` follow in their slots.
-template <bool AK, bool BK>
+template <bool AK, bool BK, int NFB>
 struct ReadPlan {
-  static constexpr int RA = AK ? 2 : 1, RB = BK ? 2 : 1, PER = RA + RB, NR = 4 * PER;
+  static constexpr int RA = AK ? 2 : 1, RB = BK ? 2 : 1;
+  static constexpr int NR = 4 * RA + NFB * RB;
+  static constexpr int NM = 4 * NFB;  // MFMAs per region
+  // Reads of fragment i (A, then B while i < NFB), and the first read slot of fragment i.
+  static constexpr int per(int i) { return RA + (i < NFB ? RB : 0); }
+  static constexpr int start(int i) { return i == 0 ? 0 : start(i - 1) + per(i - 1); }
+  static constexpr int frag(int I, int i = 0) { return I < start(i + 1) ? i : frag(I, i + 1); }
 };
 
-template <int D, int QB, int I, bool AK, bool BK, class LA, class LB>
+template <int D, int QB, int I, bool AK, bool BK, int NFB, class LA, class LB>
 __device__ __forceinline__ void region_mem(const LA& la, const LB& lb, const uint16_t* st,
-                                           const Frag<AK, BK>& f, int kk, bf16x8 (&na)[4],
-                                           bf16x8 (&nb)[4], v4i16 (&tmp)[4], uint16_t* dst,
+                                           const Frag<AK, BK, NFB>& f, int kk, bf16x8 (&na)[4],
+                                           bf16x8 (&nb)[NFB], v4i16 (&tmp)[4], uint16_t* dst,
                                            int kstep) {
-  using P = ReadPlan<AK, BK>;
+  using P = ReadPlan<AK, BK, NFB>;
   if constexpr (I < P::NR) {
-    constexpr int i = I / P::PER, r = I % P::PER;
+    constexpr int i = P::frag(I), r = I - P::start(i);
     if constexpr (r < P::RA) {
       if constexpr (!AK) {
         na[i] = f.a.read(st, kk, i);
@@ -350,23 +376,24 @@ __device__ __forceinline__ void region_mem(const LA& la, const LB& lb, const uin
       }
     }
   }
-  issue_range<QB + (I * D) / 16, QB + ((I + 1) * D) / 16>(la, lb, dst, kstep);
-  if constexpr (I + 1 < 16)
-    region_mem<D, QB, I + 1, AK, BK>(la, lb, st, f, kk, na, nb, tmp, dst, kstep);
+  issue_range<QB + (I * D) / P::NM, QB + ((I + 1) * D) / P::NM>(la, lb, dst, kstep);
+  if constexpr (I + 1 < P::NM)
+    region_mem<D, QB, I + 1, AK, BK, NFB>(la, lb, st, f, kk, na, nb, tmp, dst, kstep);
 }
 
-// One region: 16 MFMAs on (a, b); fragment reads of substep kk from stage `st` into (na, nb);
-// DMA instructions QB .. QB+D-1 of step `kstep` into stage `dst`.
-template <int D, int QB, bool AK, bool BK, class LA, class LB>
+// One region: 4 x NFB MFMAs on (a, b); fragment reads of substep kk from stage `st` into
+// (na, nb); DMA instructions QB .. QB+D-1 of step `kstep` into stage `dst`.
+template <int D, int QB, bool AK, bool BK, int NFB, class LA, class LB>
 __device__ __forceinline__ void region(const LA& la, const LB& lb, const bf16x8 (&a)[4],
-                                       const bf16x8 (&b)[4], const uint16_t* st,
-                                       const Frag<AK, BK>& f, int kk, bf16x8 (&na)[4],
-                                       bf16x8 (&nb)[4], uint16_t* dst, int kstep,
-                                       f32x16 (&acc)[4][4]) {
+                                       const bf16x8 (&b)[NFB], const uint16_t* st,
+                                       const Frag<AK, BK, NFB>& f, int kk, bf16x8 (&na)[4],
+                                       bf16x8 (&nb)[NFB], uint16_t* dst, int kstep,
+                                       f32x16 (&acc)[4][NFB]) {
+  using P = ReadPlan<AK, BK, NFB>;
   v4i16 tmp[4];
-  mfmas<0, 16>(a, b, acc);
-  region_mem<D, QB, 0, AK, BK>(la, lb, st, f, kk, na, nb, tmp, dst, kstep);
-  region_slot<D, ReadPlan<AK, BK>::NR, 0>();
+  mfmas<0, P::NM, NFB>(a, b, acc);
+  region_mem<D, QB, 0, AK, BK, NFB>(la, lb, st, f, kk, na, nb, tmp, dst, kstep);
+  region_slot<D, P::NR, 0, P::NM>();
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -383,22 +410,24 @@ __device__ __forceinline__ void region(const LA& la, const LB& lb, const bf16x8 
 // steps past the end are clamped to the last step (an in-bounds reload into a stage that is
 // never read again), which keeps every iteration the same shape. All DMA is drained before
 // returning.
-template <class LA, class LB>
+template <class LA, class LB, int NFB = 4>
 __device__ __forceinline__ void mainloop(const LA& la, const LB& lb, int ks0, int ks1,
-                                         uint16_t* smem, f32x16 (&acc)[4][4]) {
-  constexpr bool AK = !__is_same(LA, Loader), BK = !__is_same(LB, Loader);
-  constexpr int NQ = 2 * NI, Q4 = NI, Q1 = NI;  // loads per step: 8 in R4, 8 in R1
+                                         uint16_t* smem, f32x16 (&acc)[4][NFB]) {
+  constexpr bool AK = LA::KMAJOR, BK = LB::KMAJOR;
+  static_assert(LA::NIW == LB::NIW, "both operands take the same loads per wave");
+  constexpr int NIW = LA::NIW;
+  constexpr int NQ = 2 * NIW, Q4 = NIW, Q1 = NIW;  // loads per step: NIW in R4, NIW in R1
   const int n = ks1 - ks0;
   if (n <= 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  Frag<AK, BK> f;
+  Frag<AK, BK, NFB> f;
   f.init(wave & 1, wave >> 1, lane);
   const int k1 = ks0 + (1 < n ? 1 : 0);
   issue_range<0, NQ>(la, lb, smem, ks0);
   issue_range<0, Q4>(la, lb, smem + 2 * STAGE, k1);
   wait_vmem_le<Q4>();
   lds_barrier();
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  bf16x8 a0[4], b0[NFB], a1[4], b1[NFB];
   load_frag(smem, smem + STAGE, f, 0, a0, b0);
   for (int s = 0; s < n; ++s) {
     uint16_t* cur = smem + (s & 1) * 2 * STAGE;
