@@ -312,8 +312,8 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
 
 // ------------------------------------------------------------------------------------
 // Cross-tile combine, in vocabulary-tile order: chain c of 16 folds tiles c, c+16, ... of a row,
-// then the row's 16 chains are folded in order c = 0..15. A workgroup takes 16 rows x 16 chains
-// (thread = chain * 16 + row), so the 4096 rows of a chunk spread over 256 workgroups; the
+// then the row's 16 chains are folded in order c = 0..15. A workgroup takes 32 rows x 16 chains
+// (thread = chain * 32 + row), so the 4096 rows of a chunk spread over 128 workgroups; the
 // arithmetic of a row does not depend on that grouping. With d_k = m_k - M:
 // S = sum_k s_k e^{d_k}, Q = sum_k e^{d_k}(q_k + s_k d_k log2 e); lse = M + ln S and
 // entropy = ln S - ln2 * Q / S. An empty shard gives lse = -inf, entropy 0, target logit 0,
@@ -334,7 +334,9 @@ __device__ __forceinline__ void fold(float& M, float& S, float& Q, float m, floa
   M = N;
 }
 
-constexpr int COMBINE_ROWS = 16, COMBINE_CHAINS = 16;
+// 32 rows: a wave's loads of one partial are 32 consecutive floats, a whole 128-byte line
+// (with 16 rows two workgroups each fetched half of every line: 70 MB for 29 MB of partials).
+constexpr int COMBINE_ROWS = 32, COMBINE_CHAINS = 16;
 
 __global__ __launch_bounds__(COMBINE_ROWS * COMBINE_CHAINS) void k_combine(CombineArgs a) {
   __shared__ float rm[COMBINE_CHAINS][COMBINE_ROWS], rs[COMBINE_CHAINS][COMBINE_ROWS],
