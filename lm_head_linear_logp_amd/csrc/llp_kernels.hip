@@ -908,7 +908,7 @@ template <bool OVERWRITE>
 __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dw(DwArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
   int mt, nt;
-  vocab_token_tile(xcd_remap(blockIdx.x, gridDim.x), a.ntm, a.ntn, mt, nt);
+  vocab_token_tile<4>(xcd_remap(blockIdx.x, gridDim.x), a.ntm, a.ntn, mt, nt);
   const int Ts = *a.count;
   if (!OVERWRITE && Ts <= 0) return;
   const int m0 = mt * BM, n0 = nt * BN;
