@@ -97,16 +97,17 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][NFB]) {
 // row: one whole L2 line, so a load instruction's requests are full lines; with 64-byte row
 // pieces the L1's request rate, not bandwidth, caps the stream below what the MFMAs need).
 // NST = 2 LDS stages of 2 x 32 KiB. One instruction moves 64 lanes x 16 bytes into a
-// contiguous 1 KiB LDS window in lane order: 8 rows of 8 chunks. Wave w fills rows
-// 64w .. 64w+63 of each operand with 8 instructions; lane i of instruction u lands in row
-// 64w + 8u + i/8 at slot i%8 and so fetches that row's logical chunk (i%8) ^ swz8(row).
+// contiguous 1 KiB LDS window in lane order: 8 rows of 8 chunks. With NW waves, wave w fills
+// rows R w .. R w + R - 1 (R = 256 / NW) of each operand with R / 8 instructions; lane i of
+// instruction u lands in row R w + 8u + i/8 at slot i%8 and so fetches that row's logical
+// chunk (i%8) ^ swz8(row).
 // swz8 puts 8 (and 16) consecutive rows reading one logical chunk on distinct banks.
 // ------------------------------------------------------------------------------------
 namespace dma {
 
 constexpr int BKD = 64;
 constexpr int NST = 2;
-constexpr int NI = 8;            // load instructions per wave per operand per step
+constexpr int NI = 8;            // load instructions per wave per operand per step, 4 waves
 constexpr int STAGE = BM * BKD;  // bf16 elements per operand per stage
 constexpr int LDS_BYTES = NST * 2 * STAGE * 2;
 
@@ -404,11 +405,12 @@ __device__ __forceinline__ void region(const LA& la, const LB& lb, const bf16x8 
 // (row-major, K-contiguous) or LoaderK (K-major); the fragment layout follows.
 // Step s (stage s%2) runs four 16-deep substeps in four branch-free regions; fragments
 // alternate between two register sets and each region reads the next substep's:
-//   R1:     MFMAs of kk0, reads of kk1, DMA of step s+1 (its last 8 loads)
+//   R1:     MFMAs of kk0, reads of kk1, DMA of step s+1 (its last NIW loads)
 //   R2, R3: MFMAs of kk1, kk2, reads of kk2, kk3
 //   -- wait for step s+1's DMA, barrier (every wave is done reading stage s%2) --
-//   R4:     MFMAs of kk3, reads of kk0 of step s+1, DMA of step s+2 (its first 8 loads)
-// A step's 16 loads are split over two regions, one per two MFMAs: issued in one burst they
+//   R4:     MFMAs of kk3, reads of kk0 of step s+1, DMA of step s+2 (its first NIW loads)
+// A region holds 4 x NFB MFMAs. A wave's 2 NIW loads of a step (16 with 4 waves, 8 with 8)
+// are split over two regions, one per two MFMAs: issued in one burst they
 // back up the address unit, and the in-order issue stalls the MFMAs queued behind them. DMA
 // steps past the end are clamped to the last step (an in-bounds reload into a stage that is
 // never read again), which keeps every iteration the same shape. All DMA is drained before
