@@ -498,3 +498,28 @@ def test_backward_overwrite_mode(llp):
                        f["lse"], dlogp, bias_dtype=torch.float32, offset=lo, rank=1, world=2,
                        dweight=sw, dbias=sb, overwrite=True)
     assert all_zero(sw, sb, out["dhidden"])
+
+
+def test_forward_batch_size_invariance_bitwise(llp):
+    """The same rows in batches of different size get the same bits: 5700 rows over 12
+    vocabulary tiles make 276 tiles (more than one round on a 256-CU device); 700 of those rows
+    (token blocks 0-1 and 19-20 of the large batch) make 36 tiles in another order. Sampled
+    rows match the oracle."""
+    T, H, Vr, Vp, tau = 5700, 512, 3000, 3072, 0.7
+    case = synth.small_case(T, H, Vr, Vp, tau, case_id=75, mask_frac=0.1, with_bias=True,
+                            w_std=0.05)
+    say("forward batch size: T=5700 V=3000 vs 700 of its rows")
+    a = run_forward(llp, case)
+    rows = np.concatenate([np.arange(0, 350), np.arange(5000, 5350)])
+    sub = dict(case, T=rows.size, hidden=case["hidden"][rows], targets=case["targets"][rows],
+               mask=case["mask"][rows])
+    b = run_forward(llp, sub)
+    for k in ("logp", "entropy", "lse", "target_logit", "in_range"):
+        np.testing.assert_array_equal(host(a[k])[rows].view(np.uint8), host(b[k]).view(np.uint8),
+                                      err_msg=k)
+    pick = np.unique(np.concatenate([rows[::37], np.arange(4608, 5700, 97)]))
+    ref = oracle.forward(case["hidden"][pick], case["weight"], case["bias"], tau,
+                         case["targets"][pick], case["mask"][pick], Vr)
+    check_forward({k: a[k][torch.from_numpy(pick).cuda()] for k in ("logp", "entropy", "lse",
+                                                                    "in_range")},
+                  ref, case["mask"][pick], "batch size")
