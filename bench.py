@@ -236,6 +236,57 @@ def measure_next_rows(llp, logits, rids, rtg, shards, stream, busy, reps=10):
     }
 
 
+def measure_config4(llp, W, stream, busy, reps=2):
+    """Config 4 after the timed steps: 16 packed sequences (lengths U{256..7168}, the first
+    20-40% of each loss-masked), chunked at 4096 rows in order; per chunk the forward (logp),
+    then the backward with that chunk's lse, dhidden per chunk, dweight overwritten by the
+    first chunk and accumulated by the rest (one training step's gradient). Mean of `reps`
+    timed passes after one warm-up pass, each queued behind `busy`."""
+    import torch
+    import synth
+
+    log("config 4: packed variable-length forward + backward, chunks of 4096")
+    case = synth.config4_case()
+    Tp = case["T"]
+    h = torch.from_numpy(np.ascontiguousarray(case["hidden"]).view(np.int16)).view(torch.bfloat16).cuda()
+    tg = torch.from_numpy(case["targets"]).cuda()
+    mk = torch.from_numpy(case["mask"]).cuda()
+    dl = torch.from_numpy(case["dlogp"]).cuda()
+    scored = int(case["mask"].sum())
+    del case
+    dH = torch.empty((Tp, H), dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty((VP, H), dtype=torch.float32, device="cuda")
+    chunks = [(c0, min(Tp, c0 + T)) for c0 in range(0, Tp, T)]
+
+    def one_pass():
+        for i, (c0, c1) in enumerate(chunks):
+            o = llp.forward(h[c0:c1], W, tg[c0:c1], temperature=TAU, loss_mask=mk[c0:c1],
+                            real_vocab=VR, padded_vocab=VP, want_entropy=False)
+            llp.backward(h[c0:c1], W, tg[c0:c1], o["lse"], dl[c0:c1], temperature=TAU,
+                         loss_mask=mk[c0:c1], real_vocab=VR, padded_vocab=VP, dweight=dW,
+                         dhidden=dH[c0:c1], overwrite=(i == 0))
+
+    one_pass()
+    torch.cuda.synchronize()
+    busy()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        one_pass()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flop = 4.0 * 2.0 * H * VR * scored   # forward + the backward's three products
+    del h, tg, mk, dl, dH, dW
+    torch.cuda.empty_cache()
+    return {"config4_forward_backward": {
+        "packed_tokens": Tp, "scored_tokens": scored, "chunks": len(chunks), "ms": ms,
+        "scored_tokens_per_s": scored / (ms * 1e-3), "tflops": flop / (ms * 1e-3) / 1e12,
+        "workload": "16 packed sequences, lengths U{256..7168}, first 20-40% of each masked, "
+                    "chunks of 4096 rows in order; forward then backward per chunk, dweight "
+                    "overwritten by the first chunk and accumulated by the rest"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,6 +438,9 @@ def main():
     }
     res.update(measure_next_rows(
         llp, logits, rids, rtg, shards, stream,
+        busy=lambda: llp.forward(h, W, tg, temperature=TAU, real_vocab=VR, padded_vocab=VP)))
+    res.update(measure_config4(
+        llp, W, stream,
         busy=lambda: llp.forward(h, W, tg, temperature=TAU, real_vocab=VR, padded_vocab=VP)))
     res.update(measure_vendor_gemm(h, W, stream))
     if not args.no_cpu_baseline:
