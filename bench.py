@@ -101,7 +101,7 @@ def ingest_pmc(fetch_csv: str, write_csv: str) -> None:
            "bytes_per_launch": (f[fwd] * fs + w[fwd] * ws) * 1024.0,
            "algorithmic_bytes_per_launch": float(2 * (VR * H + T * H) + T * 64),
            "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
-                      "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration"}
+                      "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --skip-config4 --copy-calibration"}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -294,6 +294,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2560)
+    ap.add_argument("--skip-config4", action="store_true",
+                    help="leave out the config-4 measurement (profiling runs: its chunks would "
+                         "mix other forward/backward shapes into the per-kernel averages)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy before the warm-up (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -439,9 +442,10 @@ def main():
     res.update(measure_next_rows(
         llp, logits, rids, rtg, shards, stream,
         busy=lambda: llp.forward(h, W, tg, temperature=TAU, real_vocab=VR, padded_vocab=VP)))
-    res.update(measure_config4(
-        llp, W, stream,
-        busy=lambda: llp.forward(h, W, tg, temperature=TAU, real_vocab=VR, padded_vocab=VP)))
+    if not args.skip_config4:
+        res.update(measure_config4(
+            llp, W, stream,
+            busy=lambda: llp.forward(h, W, tg, temperature=TAU, real_vocab=VR, padded_vocab=VP)))
     res.update(measure_vendor_gemm(h, W, stream))
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_rows} rows")
