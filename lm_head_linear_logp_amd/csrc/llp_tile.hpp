@@ -171,13 +171,27 @@ using Loader = LoaderT<4>;
 // and columns past the valid ones as column 0 (callers never use those values).
 __device__ __forceinline__ int fk(int r) { return 2 * (r & 3); }
 
-struct LoaderK {
+// One K-major DMA instruction (non-template, like BufRsrc): the resource is based at K step
+// `kstep`'s first row, 16 bytes per lane from byte offset voff into the LDS window at `lds`.
+__device__ __forceinline__ void loadk_issue(const uint16_t* base, int64_t ld, int kstep,
+                                            uint16_t* lds, uint32_t voff) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(base + (int64_t)kstep * BKD * ld), (short)0, (int)(BKD * ld * 2), 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+
+// With NW waves, wave w fills K-rows KR w .. KR w + KR - 1 (KR = 64 / NW) of a stage with KR / 2
+// instructions, two K-rows each.
+template <int NW>
+struct LoaderKT {
   static constexpr bool KMAJOR = true;
-  static constexpr int NIW = NI;
+  static constexpr int KR = BKD / NW;  // K-rows per wave
+  static constexpr int NIW = KR / 2;
   const uint16_t* base;  // row 0, first column of the tile
   int64_t ld;            // row stride (elements)
   int maxrow;            // last readable row
-  int r0;                // this lane's K-row for u = 0 within a step: 16w + lane/32
+  int r0;                // this lane's K-row for u = 0 within a step: KR w + lane/32
   int cb[2];             // byte offset of this lane's chunk within a K-row, by u parity
 
   __device__ __forceinline__ void init(const uint16_t* b, int64_t ld_, int maxrow_, int ncols) {
@@ -185,7 +199,7 @@ struct LoaderK {
     ld = ld_;
     maxrow = maxrow_;
     const int lane = threadIdx.x & 63;
-    r0 = 16 * (threadIdx.x >> 6) + (lane >> 5);
+    r0 = KR * (threadIdx.x >> 6) + (lane >> 5);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       int c = (lane & 31) ^ fk(2 * p + (lane >> 5));
@@ -197,13 +211,10 @@ struct LoaderK {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rlim = maxrow - kstep * BKD;
     const int r = r0 + 2 * u < rlim ? r0 + 2 * u : rlim;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(base + (int64_t)kstep * BKD * ld), (short)0, (int)(BKD * ld * 2), 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(stage + (16 * w + 2 * u) * BM), 16,
-        (uint32_t)(r * (int)ld * 2 + cb[u & 1]), 0, 0, 0);
+    loadk_issue(base, ld, kstep, stage + (KR * w + 2 * u) * BM, (uint32_t)(r * (int)ld * 2 + cb[u & 1]));
   }
 };
+using LoaderK = LoaderKT<4>;
 
 // Fragment addressing of one operand in a stage. Row-major (K-contiguous) operands read one
 // 16-byte chunk per fragment; K-major operands build it from two ds_read_b64_tr_b16, which
@@ -236,14 +247,15 @@ struct FragOp<false, NF> {
   }
 };
 
-template <>
-struct FragOp<true, 4> {
-  int off[4];  // bytes
+// NF fragments of 32 columns from column 32 NF wx of the stage.
+template <int NF>
+struct FragOp<true, NF> {
+  int off[NF];  // bytes
   __device__ __forceinline__ void init(int wx, int lane) {
     const int g = lane >> 4, j = (lane >> 2) & 3, t = lane & 3;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int chunk = wx * 16 + 4 * i + 2 * (g & 1) + (t >> 1);
+    for (int i = 0; i < NF; ++i) {
+      const int chunk = wx * 4 * NF + 4 * i + 2 * (g & 1) + (t >> 1);
       off[i] = (8 * (g >> 1) + j) * (BM * 2) + 16 * (chunk ^ (2 * j)) + 8 * (t & 1);
     }
   }
