@@ -254,7 +254,7 @@ def test_topp_row_position_invariance_bitwise(llp):
     takes the fallback), masked rows, empty rows and an invalid id are included, over a
     full-vocabulary call and a shard."""
     x, ids, tg = topp_small()
-    T = 32768 + 13
+    T = 65536 + 13
     idx = np.arange(T) % x.shape[0]
     X, I, G = dev(x[idx]), ids[idx].copy(), tg[idx]
     I[7, 2] = 640                          # padded id: invalid, ignored
@@ -268,7 +268,7 @@ def test_topp_row_position_invariance_bitwise(llp):
                   world=1 if (lo, hi) == (0, 640) else 4, local_size=hi - lo)
         st = torch.zeros(1, dtype=torch.int32, device="cuda")
         big = llp.top_p_replay(X[:, lo:hi], Id, Gd, loss_mask=Md, status=st, **kw)
-        cuts = [0, 5, 16387, 16390, T]
+        cuts = [0, 5, 16387, 16390, 50000, T]
         parts = [llp.top_p_replay(X[s:e, lo:hi], Id[s:e], Gd[s:e], loss_mask=Md[s:e], **kw)
                  for s, e in zip(cuts[:-1], cuts[1:])]
         dense = llp.keep_mask_replay(X[:, lo:hi], Kd[:, lo:hi], Gd, loss_mask=Md, **kw)
