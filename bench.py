@@ -306,8 +306,9 @@ def main():
         ingest_pmc(*args.ingest_pmc)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures the one-GPU hot path only; runs on more than one GPU are not "
-              "part of this build (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures the hot path on one GPU only: the library has no multi-GPU "
+              "path (vocabulary shards run one after another on one GPU and are merged in "
+              "rank order by llp_merge).", file=sys.stderr)
         sys.exit(2)
 
     import torch
