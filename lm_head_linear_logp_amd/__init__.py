@@ -67,7 +67,11 @@ def _stream_ptr(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _need(t, name, dtype, ndim, device):
+def _need(t, name, dtype, ndim, device, shape=None):
+    """Type, rank, device and last-dimension contiguity of a tensor the library reads or
+    writes through a raw pointer; with `shape`, also its exact shape (None entries are free).
+    The kernels index by T, H and local_size, so a short tensor would be an out-of-bounds
+    device access: every mismatch is refused here, before anything is enqueued."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
@@ -76,8 +80,25 @@ def _need(t, name, dtype, ndim, device):
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
     if t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
-    if ndim >= 1 and t.stride(-1) != 1:
+    if shape is not None:
+        for i, n in enumerate(shape):
+            if n is not None and t.shape[i] != n:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected "
+                                 f"{tuple('*' if x is None else x for x in shape)}")
+    if ndim >= 1 and t.numel() > 0 and t.stride(-1) != 1:
         raise ValueError(f"{name} must be contiguous in its last dimension")
+
+
+def _vec(t, name, dtype, n, device):
+    """A contiguous 1-d tensor of exactly n elements."""
+    _need(t, name, dtype, 1, device, (n,))
+
+
+def _status(status, device):
+    if status is not None:
+        _need(status, "status", torch.int32, 1, device)
+        if status.numel() < 1:
+            raise ValueError("status must hold at least one int32")
 
 
 def _request(hidden, weight, target_ids, temperature, bias, loss_mask, cu_seqlens, offset,
@@ -85,12 +106,10 @@ def _request(hidden, weight, target_ids, temperature, bias, loss_mask, cu_seqlen
     dev = hidden.device
     _need(hidden, "hidden", torch.bfloat16, 2, dev)
     _need(weight, "weight", torch.bfloat16, 2, dev)
-    _need(target_ids, "target_ids", torch.int64, 1, dev)
     T, H = hidden.shape
+    _vec(target_ids, "target_ids", torch.int64, T, dev)
     if weight.shape[1] != H:
         raise ValueError(f"weight is {tuple(weight.shape)}, hidden size is {H}")
-    if target_ids.shape[0] != T:
-        raise ValueError("target_ids length differs from the number of rows")
     if padded_vocab is None:
         padded_vocab = weight.shape[0] if world == 1 else None
     if real_vocab is None:
@@ -103,10 +122,9 @@ def _request(hidden, weight, target_ids, temperature, bias, loss_mask, cu_seqlen
     req.proj.weight = _ptr(weight)
     req.proj.weight_stride = weight.stride(0) if weight.shape[0] > 0 else H
     if bias is not None:
-        if bias.dtype not in (torch.bfloat16, torch.float32) or bias.dim() != 1:
-            raise TypeError("bias must be a 1-d bf16 or fp32 tensor")
-        if bias.shape[0] != weight.shape[0] or bias.device != dev or bias.stride(0) != 1:
-            raise ValueError("bias must be contiguous with one value per weight row")
+        if not isinstance(bias, torch.Tensor) or bias.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("bias must be a bf16 or fp32 tensor")
+        _vec(bias, "bias", bias.dtype, weight.shape[0], dev)
         req.proj.bias = _ptr(bias)
         req.proj.bias_dtype = A.LLP_DTYPE_F32 if bias.dtype == torch.float32 else A.LLP_DTYPE_BF16
     req.proj.hidden_size = H
@@ -118,20 +136,19 @@ def _request(hidden, weight, target_ids, temperature, bias, loss_mask, cu_seqlen
     req.vocab.world = int(world)
     req.layout.num_tokens = T
     if loss_mask is not None:
-        _need(loss_mask, "loss_mask", torch.uint8, 1, dev)
-        if loss_mask.shape[0] != T:
-            raise ValueError("loss_mask length differs from the number of rows")
+        _vec(loss_mask, "loss_mask", torch.uint8, T, dev)
         req.layout.loss_mask = _ptr(loss_mask)
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+        if cu_seqlens.shape[0] < 1:
+            raise ValueError("cu_seqlens needs at least one entry")
         req.layout.cu_seqlens = _ptr(cu_seqlens)
         req.layout.num_seqs = cu_seqlens.shape[0] - 1
     req.target_ids = _ptr(target_ids)
     req.temperature = float(temperature)
     req.flags = A.LLP_FLAG_WANT_ENTROPY if want_entropy else 0
-    if status is not None:
-        _need(status, "status", torch.int32, 1, dev)
-        req.status_word = _ptr(status)
+    _status(status, dev)
+    req.status_word = _ptr(status)
     return req
 
 
@@ -148,6 +165,23 @@ def _workspace(req, op, dev, workspace):
     return workspace
 
 
+def _partials_out(out, T, dev, want_entropy, with_logp_required=False):
+    """Checks a caller-supplied partials dict (target_logit, in_range, lse, entropy, logp)."""
+    _vec(out["target_logit"], "out['target_logit']", torch.float32, T, dev)
+    _vec(out["in_range"], "out['in_range']", torch.uint8, T, dev)
+    _vec(out["lse"], "out['lse']", torch.float32, T, dev)
+    ent = out.get("entropy")
+    if want_entropy:
+        if ent is None:
+            raise ValueError("out['entropy'] is required when the entropy is wanted")
+        _vec(ent, "out['entropy']", torch.float32, T, dev)
+    elif ent is not None:
+        raise ValueError("out['entropy'] given but the entropy is not wanted")
+    lp = out.get("logp")
+    if lp is not None or with_logp_required:
+        _vec(lp, "out['logp']", torch.float32, T, dev)
+
+
 def forward(hidden: torch.Tensor, weight: torch.Tensor, target_ids: torch.Tensor, *,
             temperature: float, bias: Optional[torch.Tensor] = None,
             loss_mask: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
@@ -158,10 +192,14 @@ def forward(hidden: torch.Tensor, weight: torch.Tensor, target_ids: torch.Tensor
     """llp_forward on one shard. Returns target_logit, in_range, lse, entropy, logp (device
     tensors of length T; entropy None unless want_entropy). For world == 1, logp/entropy are
     final; otherwise pass the shards' results to ``merge``."""
-    open(hidden.device.index)
     req = _request(hidden, weight, target_ids, temperature, bias, loss_mask, cu_seqlens, offset,
                    real_vocab, padded_vocab, rank, world, want_entropy, status)
     dev, T = hidden.device, hidden.shape[0]
+    if out is not None:
+        _partials_out(out, T, dev, want_entropy)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1, dev)
+    open(dev.index)
     if out is None:
         out = dict(target_logit=torch.empty(T, dtype=torch.float32, device=dev),
                    in_range=torch.empty(T, dtype=torch.uint8, device=dev),
@@ -182,27 +220,32 @@ def merge(parts: Sequence[dict], *, loss_mask: Optional[torch.Tensor] = None,
     world = len(parts)
     if world < 1:
         raise ValueError("merge needs at least one shard")
+    if world > A.LLP_MAX_WORLD:
+        raise ValueError(f"merge takes at most {A.LLP_MAX_WORLD} shards")
+    if not isinstance(parts[0].get("lse"), torch.Tensor):
+        raise TypeError("parts[0]['lse'] must be a torch.Tensor")
     dev = parts[0]["lse"].device
-    T = parts[0]["lse"].shape[0]
-    open(dev.index)
+    T = parts[0]["lse"].shape[0] if parts[0]["lse"].dim() == 1 else -1
     arr = (A.llp_partials * world)()
     for r, p in enumerate(parts):
         for k, dt in (("target_logit", torch.float32), ("in_range", torch.uint8),
                       ("lse", torch.float32)):
-            _need(p[k], f"parts[{r}].{k}", dt, 1, dev)
-            if p[k].shape[0] != T:
-                raise ValueError(f"parts[{r}].{k} length differs")
+            _vec(p[k], f"parts[{r}]['{k}']", dt, T, dev)
         ent = p.get("entropy") if want_entropy else None
+        if want_entropy:
+            if ent is None:
+                raise ValueError(f"parts[{r}]['entropy'] is required for the merged entropy")
+            _vec(ent, f"parts[{r}]['entropy']", torch.float32, T, dev)
         arr[r] = A.llp_partials(_ptr(p["target_logit"]), _ptr(p["in_range"]), _ptr(p["lse"]),
                                 _ptr(ent), None)
+    if loss_mask is not None:
+        _vec(loss_mask, "loss_mask", torch.uint8, T, dev)
+    _status(status, dev)
+    open(dev.index)
     out = dict(logp=torch.empty(T, dtype=torch.float32, device=dev),
                lse=torch.empty(T, dtype=torch.float32, device=dev),
                entropy=torch.empty(T, dtype=torch.float32, device=dev) if want_entropy else None)
     fo = A.llp_final_out(_ptr(out["logp"]), _ptr(out["lse"]), _ptr(out["entropy"]))
-    if loss_mask is not None:
-        _need(loss_mask, "loss_mask", torch.uint8, 1, dev)
-    if status is not None:
-        _need(status, "status", torch.int32, 1, dev)
     _check(A.load().llp_merge(world, arr, T, _ptr(loss_mask), C.byref(fo), _ptr(status),
                               _stream_ptr(dev)), "llp_merge")
     return out
@@ -222,94 +265,45 @@ def backward(hidden: torch.Tensor, weight: torch.Tensor, target_ids: torch.Tenso
     dbias (fp32, accumulated; allocated when the request has a bias or want_dbias). With
     overwrite=True (LLP_FLAG_OVERWRITE_GRADS) dweight and dbias are written instead of added
     to, and a missing dweight/dbias is allocated uninitialised."""
-    open(hidden.device.index)
     req = _request(hidden, weight, target_ids, temperature, bias, loss_mask, cu_seqlens, offset,
                    real_vocab, padded_vocab, rank, world, False, status)
     if overwrite:
         req.flags |= A.LLP_FLAG_OVERWRITE_GRADS
     dev = hidden.device
     T, H = hidden.shape
-    for name, t in (("lse", lse), ("dlogp", dlogp)):
-        _need(t, name, torch.float32, 1, dev)
+    V = weight.shape[0]
+    _vec(lse, "lse", torch.float32, T, dev)
+    _vec(dlogp, "dlogp", torch.float32, T, dev)
     if dentropy is not None:
-        _need(dentropy, "dentropy", torch.float32, 1, dev)
-        _need(entropy, "entropy", torch.float32, 1, dev)
+        if entropy is None:
+            raise ValueError("dentropy needs the merged entropy")
+        _vec(dentropy, "dentropy", torch.float32, T, dev)
+        _vec(entropy, "entropy", torch.float32, T, dev)
+    if dhidden is not None:
+        _need(dhidden, "dhidden", torch.bfloat16, 2, dev, (T, H))
+    if dweight is not None:
+        _need(dweight, "dweight", torch.float32, 2, dev, (V, H))
+    if want_dbias is None:
+        want_dbias = bias is not None or dbias is not None
+    if dbias is not None:
+        _vec(dbias, "dbias", torch.float32, V, dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1, dev)
+    open(dev.index)
     if dhidden is None:
         dhidden = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     alloc = torch.empty if overwrite else torch.zeros
     if dweight is None:
         dweight = alloc(weight.shape, dtype=torch.float32, device=dev)
-    _need(dhidden, "dhidden", torch.bfloat16, 2, dev)
-    _need(dweight, "dweight", torch.float32, 2, dev)
-    if want_dbias is None:
-        want_dbias = bias is not None
     if dbias is None and want_dbias:
-        dbias = alloc(weight.shape[0], dtype=torch.float32, device=dev)
+        dbias = alloc(V, dtype=torch.float32, device=dev)
     bi = A.llp_bwd_in(_ptr(lse), _ptr(dlogp), _ptr(dentropy), _ptr(entropy))
     bo = A.llp_bwd_out(_ptr(dhidden), dhidden.stride(0) if T > 0 else H, _ptr(dweight),
-                       dweight.stride(0) if weight.shape[0] > 0 else H, _ptr(dbias))
+                       dweight.stride(0) if V > 0 else H, _ptr(dbias))
     ws = _workspace(req, A.LLP_OP_BACKWARD, dev, workspace)
     _check(A.load().llp_backward(C.byref(req), C.byref(bi), C.byref(bo), _ptr(ws), ws.numel(),
                                  _stream_ptr(dev)), "llp_backward")
     return dict(dhidden=dhidden, dweight=dweight, dbias=dbias)
-
-
-def top_p_replay(logits: torch.Tensor, replay_ids: torch.Tensor, target_ids: torch.Tensor, *,
-                 temperature: float, offset: int = 0, real_vocab: Optional[int] = None,
-                 padded_vocab: Optional[int] = None, rank: int = 0, world: int = 1,
-                 loss_mask: Optional[torch.Tensor] = None, processed_logprobs: bool = True,
-                 status: Optional[torch.Tensor] = None, local_size: Optional[int] = None) -> dict:
-    """llp_top_p_replay on one shard's local logits [T, local_size] (fp32 or bf16; a strided
-    view of a wider logits tensor is fine). Returns target_logit, in_range, lse, logp."""
-    dev = logits.device
-    open(dev.index)
-    if logits.dtype not in (torch.float32, torch.bfloat16) or logits.dim() != 2:
-        raise TypeError("logits must be a 2-d fp32 or bf16 tensor")
-    if logits.stride(1) != 1:
-        raise ValueError("logits must be contiguous in its last dimension")
-    _need(replay_ids, "replay_ids", torch.int64, 2, dev)
-    _need(target_ids, "target_ids", torch.int64, 1, dev)
-    T = replay_ids.shape[0]
-    if local_size is None:
-        local_size = logits.shape[1]
-    if padded_vocab is None:
-        padded_vocab = local_size if world == 1 else None
-    if real_vocab is None:
-        real_vocab = padded_vocab
-    if padded_vocab is None:
-        raise ValueError("padded_vocab is required for a vocabulary shard (world > 1)")
-    req = A.llp_topp_request()
-    req.logits = _ptr(logits)
-    req.logits_dtype = A.LLP_DTYPE_F32 if logits.dtype == torch.float32 else A.LLP_DTYPE_BF16
-    req.num_replay = replay_ids.shape[1]
-    req.logits_stride = logits.stride(0) if logits.shape[0] > 0 else local_size
-    req.num_tokens = T
-    req.vocab.offset = int(offset)
-    req.vocab.local_size = int(local_size)
-    req.vocab.real_vocab = int(real_vocab)
-    req.vocab.padded_vocab = int(padded_vocab)
-    req.vocab.rank = int(rank)
-    req.vocab.world = int(world)
-    req.replay_ids = _ptr(replay_ids)
-    req.replay_stride = replay_ids.stride(0) if T > 0 else replay_ids.shape[1]
-    req.target_ids = _ptr(target_ids)
-    if loss_mask is not None:
-        _need(loss_mask, "loss_mask", torch.uint8, 1, dev)
-        req.loss_mask = _ptr(loss_mask)
-    req.temperature = float(temperature)
-    req.processed_logprobs = 1 if processed_logprobs else 0
-    if status is not None:
-        _need(status, "status", torch.int32, 1, dev)
-        req.status_word = _ptr(status)
-    out = dict(target_logit=torch.empty(T, dtype=torch.float32, device=dev),
-               in_range=torch.empty(T, dtype=torch.uint8, device=dev),
-               lse=torch.empty(T, dtype=torch.float32, device=dev), entropy=None,
-               logp=torch.empty(T, dtype=torch.float32, device=dev))
-    o = A.llp_partials(_ptr(out["target_logit"]), _ptr(out["in_range"]), _ptr(out["lse"]), None,
-                       _ptr(out["logp"]))
-    _check(A.load().llp_top_p_replay(C.byref(req), C.byref(o), _stream_ptr(dev)),
-           "llp_top_p_replay")
-    return out
 
 
 def _vocab(req_vocab, offset, local_size, real_vocab, padded_vocab, rank, world):
@@ -327,13 +321,66 @@ def _vocab(req_vocab, offset, local_size, real_vocab, padded_vocab, rank, world)
     req_vocab.world = int(world)
 
 
-def _logits_view(logits, local_size):
-    if logits.dtype not in (torch.float32, torch.bfloat16) or logits.dim() != 2:
-        raise TypeError("logits must be a 2-d fp32 or bf16 tensor")
-    if logits.stride(1) != 1:
-        raise ValueError("logits must be contiguous in its last dimension")
+def _logits_view(logits, T, local_size, dev):
+    """A shard's local logits [T, >= local_size] (fp32 or bf16, contiguous rows): returns the
+    ABI dtype code, the row stride and local_size (default: the view's width)."""
+    if not isinstance(logits, torch.Tensor) or logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("logits must be an fp32 or bf16 tensor")
+    _need(logits, "logits", logits.dtype, 2, dev, (T, None))
+    if local_size is None:
+        local_size = logits.shape[1]
+    if not 0 <= int(local_size) <= logits.shape[1]:
+        raise ValueError(f"local_size {local_size} outside the logits width {logits.shape[1]}")
     dt = A.LLP_DTYPE_F32 if logits.dtype == torch.float32 else A.LLP_DTYPE_BF16
-    return dt, (logits.stride(0) if logits.shape[0] > 0 else local_size)
+    return dt, (logits.stride(0) if T > 0 else int(local_size)), int(local_size)
+
+
+def _partials_alloc(T, dev, want_entropy):
+    return dict(target_logit=torch.empty(T, dtype=torch.float32, device=dev),
+                in_range=torch.empty(T, dtype=torch.uint8, device=dev),
+                lse=torch.empty(T, dtype=torch.float32, device=dev),
+                entropy=torch.empty(T, dtype=torch.float32, device=dev) if want_entropy else None,
+                logp=torch.empty(T, dtype=torch.float32, device=dev))
+
+
+def top_p_replay(logits: torch.Tensor, replay_ids: torch.Tensor, target_ids: torch.Tensor, *,
+                 temperature: float, offset: int = 0, real_vocab: Optional[int] = None,
+                 padded_vocab: Optional[int] = None, rank: int = 0, world: int = 1,
+                 loss_mask: Optional[torch.Tensor] = None, processed_logprobs: bool = True,
+                 status: Optional[torch.Tensor] = None, local_size: Optional[int] = None) -> dict:
+    """llp_top_p_replay on one shard's local logits [T, local_size] (fp32 or bf16; a strided
+    view of a wider logits tensor is fine). Returns target_logit, in_range, lse, logp."""
+    dev = logits.device
+    if not isinstance(replay_ids, torch.Tensor):
+        raise TypeError("replay_ids must be a torch.Tensor")
+    _need(replay_ids, "replay_ids", torch.int64, 2, dev)
+    T = replay_ids.shape[0]
+    _vec(target_ids, "target_ids", torch.int64, T, dev)
+    dt, ld, local_size = _logits_view(logits, T, local_size, dev)
+    req = A.llp_topp_request()
+    req.logits = _ptr(logits)
+    req.logits_dtype = dt
+    req.num_replay = replay_ids.shape[1]
+    req.logits_stride = ld
+    req.num_tokens = T
+    _vocab(req.vocab, offset, local_size, real_vocab, padded_vocab, rank, world)
+    req.replay_ids = _ptr(replay_ids)
+    req.replay_stride = replay_ids.stride(0) if T > 0 else replay_ids.shape[1]
+    req.target_ids = _ptr(target_ids)
+    if loss_mask is not None:
+        _vec(loss_mask, "loss_mask", torch.uint8, T, dev)
+        req.loss_mask = _ptr(loss_mask)
+    req.temperature = float(temperature)
+    req.processed_logprobs = 1 if processed_logprobs else 0
+    _status(status, dev)
+    req.status_word = _ptr(status)
+    open(dev.index)
+    out = _partials_alloc(T, dev, False)
+    o = A.llp_partials(_ptr(out["target_logit"]), _ptr(out["in_range"]), _ptr(out["lse"]), None,
+                       _ptr(out["logp"]))
+    _check(A.load().llp_top_p_replay(C.byref(req), C.byref(o), _stream_ptr(dev)),
+           "llp_top_p_replay")
+    return out
 
 
 def forward_logits(logits: torch.Tensor, target_ids: torch.Tensor, *, temperature: float,
@@ -346,34 +393,32 @@ def forward_logits(logits: torch.Tensor, target_ids: torch.Tensor, *, temperatur
     """llp_forward_logits on one shard's unscaled local logits [T, local_size] (fp32 or bf16;
     a strided view of a wider tensor is fine). Returns the partials of ``forward``."""
     dev = logits.device
-    open(dev.index)
+    if not isinstance(target_ids, torch.Tensor):
+        raise TypeError("target_ids must be a torch.Tensor")
     _need(target_ids, "target_ids", torch.int64, 1, dev)
     T = target_ids.shape[0]
-    if local_size is None:
-        local_size = logits.shape[1]
+    dt, ld, local_size = _logits_view(logits, T, local_size, dev)
     req = A.llp_logits_request()
     req.logits = _ptr(logits)
-    req.logits_dtype, req.logits_stride = _logits_view(logits, local_size)
+    req.logits_dtype, req.logits_stride = dt, ld
     _vocab(req.vocab, offset, local_size, real_vocab, padded_vocab, rank, world)
     req.layout.num_tokens = T
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+        if cu_seqlens.shape[0] < 1:
+            raise ValueError("cu_seqlens needs at least one entry")
         req.layout.cu_seqlens = _ptr(cu_seqlens)
         req.layout.num_seqs = cu_seqlens.shape[0] - 1
     if loss_mask is not None:
-        _need(loss_mask, "loss_mask", torch.uint8, 1, dev)
+        _vec(loss_mask, "loss_mask", torch.uint8, T, dev)
         req.layout.loss_mask = _ptr(loss_mask)
     req.target_ids = _ptr(target_ids)
     req.temperature = float(temperature)
     req.flags = A.LLP_FLAG_WANT_ENTROPY if want_entropy else 0
-    if status is not None:
-        _need(status, "status", torch.int32, 1, dev)
-        req.status_word = _ptr(status)
-    out = dict(target_logit=torch.empty(T, dtype=torch.float32, device=dev),
-               in_range=torch.empty(T, dtype=torch.uint8, device=dev),
-               lse=torch.empty(T, dtype=torch.float32, device=dev),
-               entropy=torch.empty(T, dtype=torch.float32, device=dev) if want_entropy else None,
-               logp=torch.empty(T, dtype=torch.float32, device=dev))
+    _status(status, dev)
+    req.status_word = _ptr(status)
+    open(dev.index)
+    out = _partials_alloc(T, dev, want_entropy)
     o = A.llp_partials(_ptr(out["target_logit"]), _ptr(out["in_range"]), _ptr(out["lse"]),
                        _ptr(out["entropy"]), _ptr(out["logp"]))
     _check(A.load().llp_forward_logits(C.byref(req), C.byref(o), _stream_ptr(dev)),
@@ -391,33 +436,32 @@ def keep_mask_replay(logits: torch.Tensor, keep_mask: torch.Tensor, target_ids: 
     the same shape (views of wider tensors are fine). Returns target_logit, in_range, lse,
     logp, as ``top_p_replay``."""
     dev = logits.device
-    open(dev.index)
+    if not isinstance(target_ids, torch.Tensor):
+        raise TypeError("target_ids must be a torch.Tensor")
     _need(target_ids, "target_ids", torch.int64, 1, dev)
-    if keep_mask.dtype != torch.uint8 or keep_mask.dim() != 2 or keep_mask.stride(1) != 1:
-        raise TypeError("keep_mask must be a 2-d uint8 tensor contiguous in its last dimension")
     T = target_ids.shape[0]
-    if local_size is None:
-        local_size = logits.shape[1]
+    dt, ld, local_size = _logits_view(logits, T, local_size, dev)
+    _need(keep_mask, "keep_mask", torch.uint8, 2, dev, (T, None))
+    if keep_mask.shape[1] < local_size:
+        raise ValueError(f"keep_mask width {keep_mask.shape[1]} < local_size {local_size}")
     req = A.llp_keep_mask_request()
     req.logits = _ptr(logits)
-    req.logits_dtype, req.logits_stride = _logits_view(logits, local_size)
+    req.logits_dtype, req.logits_stride = dt, ld
     req.keep_mask = _ptr(keep_mask)
-    req.keep_stride = keep_mask.stride(0) if keep_mask.shape[0] > 0 else local_size
+    req.keep_stride = keep_mask.stride(0) if T > 0 else local_size
     req.num_tokens = T
     _vocab(req.vocab, offset, local_size, real_vocab, padded_vocab, rank, world)
     req.target_ids = _ptr(target_ids)
     if loss_mask is not None:
-        _need(loss_mask, "loss_mask", torch.uint8, 1, dev)
+        _vec(loss_mask, "loss_mask", torch.uint8, T, dev)
         req.loss_mask = _ptr(loss_mask)
     req.temperature = float(temperature)
     req.processed_logprobs = 1 if processed_logprobs else 0
-    if status is not None:
-        _need(status, "status", torch.int32, 1, dev)
-        req.status_word = _ptr(status)
-    out = dict(target_logit=torch.empty(T, dtype=torch.float32, device=dev),
-               in_range=torch.empty(T, dtype=torch.uint8, device=dev),
-               lse=torch.empty(T, dtype=torch.float32, device=dev),
-               logp=torch.empty(T, dtype=torch.float32, device=dev))
+    _status(status, dev)
+    req.status_word = _ptr(status)
+    open(dev.index)
+    out = _partials_alloc(T, dev, False)
+    del out["entropy"]
     o = A.llp_partials(_ptr(out["target_logit"]), _ptr(out["in_range"]), _ptr(out["lse"]), None,
                        _ptr(out["logp"]))
     _check(A.load().llp_keep_mask_replay(C.byref(req), C.byref(o), _stream_ptr(dev)),
