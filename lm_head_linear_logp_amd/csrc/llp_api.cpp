@@ -87,8 +87,12 @@ llp_status check_request(const llp_request* req) {
   // Operand rows are addressed with 32-bit byte offsets from a tile's first row.
   LLP_CHECK(p.hidden_stride < (int64_t(1) << 23) && p.weight_stride < (int64_t(1) << 23),
             LLP_ERR_UNSUPPORTED, "hidden_stride and weight_stride must be < 2^23");
-  LLP_CHECK(T * p.hidden_stride <= (int64_t(1) << 31), LLP_ERR_UNSUPPORTED,
-            "T * hidden_stride = %lld exceeds 2^31", (long long)(T * p.hidden_stride));
+  // The fused tiles gather hidden rows through one buffer resource per tile, based at the
+  // tile's first scored row, with 32-bit byte offsets: every byte of the T rows must lie below
+  // 2^31 from the base.
+  LLP_CHECK(T * p.hidden_stride * 2 < (int64_t(1) << 31), LLP_ERR_UNSUPPORTED,
+            "hidden spans T * hidden_stride * 2 = %lld bytes; must be < 2^31",
+            (long long)(T * p.hidden_stride * 2));
   LLP_CHECK(req->vocab.local_size <= (int64_t(1) << 23) - 256, LLP_ERR_UNSUPPORTED,
             "local_size %lld exceeds 2^23 - 256", (long long)req->vocab.local_size);
   if (T > 0) {

@@ -258,8 +258,9 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][NFB], const 
 
 // Loaders of the fused tiles: weight rows v0 .. (clamped below n_real) and the scored hidden
 // rows j0 .. (clamped below the count), gathered through `scored` (ascending). The hidden
-// resource starts at the tile's first scored row; the host keeps T * hidden_stride * 2 below
-// 2^31 bytes, so every lane offset fits in 32 bits.
+// resource starts at the tile's first scored row; the host keeps all T rows within 2^31 bytes
+// (T * hidden_stride * 2 < 2^31), so every lane offset, plus the K step's scalar offset, stays
+// below 2^31 and inside the resource's range.
 template <int NW>
 __device__ __forceinline__ void weight_hidden_loaders(const uint16_t* W, int64_t ldw, int64_t n_real,
                                                       int v0, const uint16_t* h, int64_t ldh,

@@ -190,6 +190,22 @@ def test_valid_request_passes_validation():
     assert st not in (A.LLP_OK, A.LLP_ERR_INVALID_ARGUMENT) or "llp_open" in A.load().llp_last_error().decode()
 
 
+def _ws_status(T, stride):
+    r = good_request(H=256, V=1024, Vr=1000)
+    r.layout.num_tokens, r.proj.hidden_stride = T, stride
+    n = C.c_size_t()
+    return A.load().llp_workspace_bytes(C.byref(r), A.LLP_OP_FORWARD, C.byref(n))
+
+
+def test_hidden_byte_bound_is_strict():
+    """The T hidden rows must span fewer than 2^31 bytes (32-bit offsets from a tile's first
+    row): exactly 2^31 is refused, one row less is accepted."""
+    assert _ws_status(1 << 22, 256) == A.LLP_ERR_UNSUPPORTED          # 2^22 * 256 * 2 = 2^31
+    assert _ws_status((1 << 22) - 1, 256) == A.LLP_OK
+    assert _ws_status(1 << 21, 512) == A.LLP_ERR_UNSUPPORTED
+    assert _ws_status((1 << 21) - 1, 512) == A.LLP_OK
+
+
 def test_workspace_bytes_pure_function():
     lib = A.load()
     n1, n2 = C.c_size_t(), C.c_size_t()
