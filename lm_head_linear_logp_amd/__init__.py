@@ -322,17 +322,26 @@ def _vocab(req_vocab, offset, local_size, real_vocab, padded_vocab, rank, world)
 
 
 def _logits_view(logits, T, local_size, dev):
-    """A shard's local logits [T, >= local_size] (fp32 or bf16, contiguous rows): returns the
-    ABI dtype code, the row stride and local_size (default: the view's width)."""
+    """A shard's local logits [T, width] (fp32 or bf16, contiguous rows): returns the ABI dtype
+    code, the row stride and local_size (default: the view's width). The view must cover the
+    shard's real columns (checked by _covers_real once the partition is known)."""
     if not isinstance(logits, torch.Tensor) or logits.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("logits must be an fp32 or bf16 tensor")
     _need(logits, "logits", logits.dtype, 2, dev, (T, None))
     if local_size is None:
         local_size = logits.shape[1]
-    if not 0 <= int(local_size) <= logits.shape[1]:
-        raise ValueError(f"local_size {local_size} outside the logits width {logits.shape[1]}")
+    if int(local_size) < 0:
+        raise ValueError(f"local_size {local_size} < 0")
     dt = A.LLP_DTYPE_F32 if logits.dtype == torch.float32 else A.LLP_DTYPE_BF16
     return dt, (logits.stride(0) if T > 0 else int(local_size)), int(local_size)
+
+
+def _covers_real(t, name, vocab):
+    """The kernels read a row's columns below the shard's real ones only,
+    clamp(real_vocab - offset, 0, local_size): `t` must be at least that wide."""
+    n_real = min(max(vocab.real_vocab - vocab.offset, 0), vocab.local_size)
+    if t.shape[1] < n_real:
+        raise ValueError(f"{name} has {t.shape[1]} columns; the shard has {n_real} real columns")
 
 
 def _partials_alloc(T, dev, want_entropy):
@@ -364,6 +373,7 @@ def top_p_replay(logits: torch.Tensor, replay_ids: torch.Tensor, target_ids: tor
     req.logits_stride = ld
     req.num_tokens = T
     _vocab(req.vocab, offset, local_size, real_vocab, padded_vocab, rank, world)
+    _covers_real(logits, "logits", req.vocab)
     req.replay_ids = _ptr(replay_ids)
     req.replay_stride = replay_ids.stride(0) if T > 0 else replay_ids.shape[1]
     req.target_ids = _ptr(target_ids)
@@ -402,6 +412,7 @@ def forward_logits(logits: torch.Tensor, target_ids: torch.Tensor, *, temperatur
     req.logits = _ptr(logits)
     req.logits_dtype, req.logits_stride = dt, ld
     _vocab(req.vocab, offset, local_size, real_vocab, padded_vocab, rank, world)
+    _covers_real(logits, "logits", req.vocab)
     req.layout.num_tokens = T
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
@@ -442,8 +453,6 @@ def keep_mask_replay(logits: torch.Tensor, keep_mask: torch.Tensor, target_ids: 
     T = target_ids.shape[0]
     dt, ld, local_size = _logits_view(logits, T, local_size, dev)
     _need(keep_mask, "keep_mask", torch.uint8, 2, dev, (T, None))
-    if keep_mask.shape[1] < local_size:
-        raise ValueError(f"keep_mask width {keep_mask.shape[1]} < local_size {local_size}")
     req = A.llp_keep_mask_request()
     req.logits = _ptr(logits)
     req.logits_dtype, req.logits_stride = dt, ld
@@ -451,6 +460,8 @@ def keep_mask_replay(logits: torch.Tensor, keep_mask: torch.Tensor, target_ids: 
     req.keep_stride = keep_mask.stride(0) if T > 0 else local_size
     req.num_tokens = T
     _vocab(req.vocab, offset, local_size, real_vocab, padded_vocab, rank, world)
+    _covers_real(logits, "logits", req.vocab)
+    _covers_real(keep_mask, "keep_mask", req.vocab)
     req.target_ids = _ptr(target_ids)
     if loss_mask is not None:
         _vec(loss_mask, "loss_mask", torch.uint8, T, dev)

@@ -161,6 +161,14 @@ def test_forward_logits_refuses():
     with pytest.raises(REACHES_LIBRARY) as e:
         llp.forward_logits(f32(T, V), tg, temperature=0.7, local_size=V - 5)
     assert not isinstance(e.value, BAD)
+    # A shard with no real columns reads no logits: a zero-width view of it is fine.
+    with pytest.raises(REACHES_LIBRARY) as e:
+        llp.forward_logits(f32(T, 4 * V)[:, :0], tg, temperature=0.7, offset=3 * V,
+                           real_vocab=2 * V, padded_vocab=4 * V, rank=3, world=4, local_size=V)
+    assert not isinstance(e.value, BAD)
+    with pytest.raises(BAD):       # the same view for a shard that has real columns
+        llp.forward_logits(f32(T, 4 * V)[:, :0], tg, temperature=0.7, offset=V,
+                           real_vocab=2 * V, padded_vocab=4 * V, rank=1, world=4, local_size=V)
     for x, kw in [(f32(T + 1, V), {}), (f32(T - 1, V), {}), (f32(T, V), dict(local_size=V + 1)),
                   (f32(T, V), dict(loss_mask=torch.ones(T - 1, dtype=torch.uint8))),
                   (torch.zeros(T, V, dtype=torch.float16), {}),

@@ -475,3 +475,26 @@ def test_planted_mistakes_are_caught(name, mut):
         except AssertionError:
             failed += 1
     assert failed >= 1, f"planted mistake '{name}' passed every pin"
+
+
+def test_backward_vocab_subset_shard_equals_full_rows():
+    """The full-size dweight check evaluates the oracle on a gathered set of vocabulary rows
+    (every target plus others) as one shard, with targets renumbered to their position in the
+    set. That reproduces the full backward's dweight rows: G[t, v] depends on z[t, v], the
+    row's (global) lse and whether v is the row's target only."""
+    case = synth.small_case(T=40, H=64, real_vocab=300, padded_vocab=320, temperature=0.7,
+                            case_id=16, mask_frac=0.3, w_std=0.2)
+    m = case["mask"].astype(bool)
+    f = oracle.forward(case["hidden"], case["weight"], None, 0.7, case["targets"], case["mask"],
+                       300)
+    dlogp = synth.rng(16, 9).standard_normal(40) * m
+    full = oracle.backward(case["hidden"], case["weight"], None, 0.7, case["targets"],
+                           case["mask"], 0, 320, 300, f["lse"], dlogp)
+    vs = np.unique(np.concatenate([case["targets"][m], [0, 7, 150, 299]]))
+    pos = np.full(320, -1, dtype=np.int64)
+    pos[vs] = np.arange(vs.size)
+    rows = np.nonzero(m)[0]
+    sub = oracle.backward(case["hidden"][rows], case["weight"][vs], None, 0.7,
+                          pos[case["targets"][rows]], None, 0, vs.size, vs.size, f["lse"][rows],
+                          dlogp[rows])
+    np.testing.assert_allclose(sub["dweight"], full["dweight"][vs], rtol=1e-12, atol=1e-14)
