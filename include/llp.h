@@ -324,6 +324,21 @@ LLP_API llp_status llp_workspace_bytes(const llp_request* req, int32_t op, size_
 LLP_API llp_status llp_forward(const llp_request* req, const llp_partials* out,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* llp_forward without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). The
+ * workspace is a static device array of the library, 32 MiB on every device the library is
+ * opened on, held until the process ends; the call allocates nothing. Results are bitwise
+ * those of llp_forward (the same kernels).
+ *   Limit: llp_workspace_bytes(req, LLP_OP_FORWARD) must be at most 32 MiB, else
+ *   LLP_ERR_UNSUPPORTED before anything is enqueued: e.g. up to 4608 rows over a 151669-column
+ *   shard, or 18432 over a 37984-column one.
+ *   Every call on one device shares that device's array. Calls that overlap on a device (on
+ *   different streams, or from several threads without ordering) race and give wrong results:
+ *   serialize them. No part of the array needs to start at zero (a call writes every value it
+ *   reads before reading it), so nothing is cleared between calls. */
+LLP_API llp_status llp_forward_noalloc(const llp_request* req, const llp_partials* out,
+                                       void* stream);
+
 /* Rank-ordered merge of `world` shards' partials ([top-p replay, "Summary"]: rank-ordered
  * reductions, shards with no candidates handled). `parts` is a HOST array of `world` structs
  * in rank order whose fields are device arrays of length num_tokens (entropy NULL in every

@@ -16,8 +16,12 @@ import torch
 
 from . import _capi as A
 
-__all__ = ["LLPError", "open", "workspace_bytes", "forward", "merge", "backward",
-           "top_p_replay", "last_error", "STATUS_BITS", "forward_logits", "keep_mask_replay"]
+__all__ = ["LLPError", "open", "workspace_bytes", "forward", "forward_noalloc", "merge",
+           "backward", "top_p_replay", "last_error", "STATUS_BITS", "forward_logits",
+           "keep_mask_replay", "SCRATCH_BYTES"]
+
+# Size of the static device scratch llp_forward_noalloc works in (include/llp.h).
+SCRATCH_BYTES = 32 << 20
 
 STATUS_BITS = {"TARGET_OUT_OF_RANGE": A.LLP_STATUS_TARGET_OUT_OF_RANGE,
                "TARGET_NOT_FOUND": A.LLP_STATUS_TARGET_NOT_FOUND,
@@ -211,6 +215,32 @@ def forward(hidden: torch.Tensor, weight: torch.Tensor, target_ids: torch.Tensor
     ws = _workspace(req, A.LLP_OP_FORWARD, dev, workspace)
     _check(A.load().llp_forward(C.byref(req), C.byref(o), _ptr(ws), ws.numel(),
                                 _stream_ptr(dev)), "llp_forward")
+    return out
+
+
+def forward_noalloc(hidden: torch.Tensor, weight: torch.Tensor, target_ids: torch.Tensor, *,
+                    temperature: float, out: dict, bias: Optional[torch.Tensor] = None,
+                    loss_mask: Optional[torch.Tensor] = None,
+                    cu_seqlens: Optional[torch.Tensor] = None, offset: int = 0,
+                    real_vocab: Optional[int] = None, padded_vocab: Optional[int] = None,
+                    rank: int = 0, world: int = 1, want_entropy: bool = True,
+                    status: Optional[torch.Tensor] = None) -> dict:
+    """llp_forward_noalloc: ``forward`` in the library's static device scratch. The caller
+    passes the output tensors (``out``: target_logit, in_range, lse, entropy when wanted,
+    logp optional); neither this function nor the library allocates device memory, so it
+    can run where allocation is not allowed. Calls that overlap on one device race on the
+    scratch."""
+    req = _request(hidden, weight, target_ids, temperature, bias, loss_mask, cu_seqlens, offset,
+                   real_vocab, padded_vocab, rank, world, want_entropy, status)
+    dev, T = hidden.device, hidden.shape[0]
+    if not isinstance(out, dict):
+        raise TypeError("out must be a dict of output tensors")
+    _partials_out(out, T, dev, want_entropy)
+    open(dev.index)
+    o = A.llp_partials(_ptr(out["target_logit"]), _ptr(out["in_range"]), _ptr(out["lse"]),
+                       _ptr(out.get("entropy")), _ptr(out.get("logp")))
+    _check(A.load().llp_forward_noalloc(C.byref(req), C.byref(o), _stream_ptr(dev)),
+           "llp_forward_noalloc")
     return out
 
 

@@ -103,6 +103,7 @@ SIGNATURES = {
     "llp_open": (C.c_int, [C.c_int32, C.POINTER(llp_info)]),
     "llp_workspace_bytes": (C.c_int, [C.POINTER(llp_request), C.c_int32, C.POINTER(C.c_size_t)]),
     "llp_forward": (C.c_int, [C.POINTER(llp_request), C.POINTER(llp_partials), vp, C.c_size_t, vp]),
+    "llp_forward_noalloc": (C.c_int, [C.POINTER(llp_request), C.POINTER(llp_partials), vp]),
     "llp_merge": (C.c_int, [C.c_int32, C.POINTER(llp_partials), C.c_int64, vp,
                             C.POINTER(llp_final_out), vp, vp]),
     "llp_backward": (C.c_int, [C.POINTER(llp_request), C.POINTER(llp_bwd_in),

@@ -316,15 +316,20 @@ LLP_API llp_status llp_open(int32_t device, llp_info* info) {
                 prop.gcnArchName);
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) return fail(LLP_ERR_UNAVAILABLE, "hipGetDevice failed");
-  if (hipSetDevice(device) != hipSuccess)
-    return fail(LLP_ERR_UNAVAILABLE, "hipSetDevice(%d) failed", device);
-  const hipError_t pe = probe_kernels();
-  (void)hipSetDevice(cur);
-  if (pe != hipSuccess)
-    return fail(LLP_ERR_UNAVAILABLE, "kernels cannot be loaded on device %d: %s", device,
-                hipGetErrorString(pe));
   {
     std::lock_guard<std::mutex> lk(g_mu);
+    if (hipSetDevice(device) != hipSuccess)
+      return fail(LLP_ERR_UNAVAILABLE, "hipSetDevice(%d) failed", device);
+    const hipError_t pe = probe_kernels();
+    // With the device current: its copy of the static scratch of llp_forward_noalloc.
+    const hipError_t se = pe == hipSuccess ? scratch_init(device) : pe;
+    (void)hipSetDevice(cur);
+    if (pe != hipSuccess)
+      return fail(LLP_ERR_UNAVAILABLE, "kernels cannot be loaded on device %d: %s", device,
+                  hipGetErrorString(pe));
+    if (se != hipSuccess)
+      return fail(LLP_ERR_UNAVAILABLE, "static scratch not addressable on device %d: %s", device,
+                  hipGetErrorString(se));
     g_opened[device] = 1;
     g_num_cus[device] = prop.multiProcessorCount;
   }
@@ -353,8 +358,14 @@ LLP_API llp_status llp_workspace_bytes(const llp_request* req, int32_t op, size_
   return LLP_OK;
 }
 
-LLP_API llp_status llp_forward(const llp_request* req, const llp_partials* out, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward of one shard on a caller's workspace (llp_forward) or the static scratch
+// (llp_forward_noalloc): validation, then layout, fused tiles and combine on `stream`.
+llp_status forward_impl(const llp_request* req, const llp_partials* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   llp_status st = check_request(req);
   if (st != LLP_OK) return st;
   LLP_CHECK(out != nullptr, LLP_ERR_INVALID_ARGUMENT, "out is NULL");
@@ -440,6 +451,34 @@ LLP_API llp_status llp_forward(const llp_request* req, const llp_partials* out, 
   ca.out_p = out->logp;
   LLP_HIP(launch_combine(ca, w.T_cap, s), "combine kernel launch");
   return LLP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+LLP_API llp_status llp_forward(const llp_request* req, const llp_partials* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return forward_impl(req, out, workspace, workspace_bytes, stream);
+}
+
+LLP_API llp_status llp_forward_noalloc(const llp_request* req, const llp_partials* out,
+                                       void* stream) {
+  llp_status st = check_request(req);
+  if (st != LLP_OK) return st;
+  const size_t need = ws_layout(req->layout.num_tokens, local_real(req->vocab),
+                                req->proj.hidden_size, LLP_OP_FORWARD).total;
+  LLP_CHECK(need <= SCRATCH_BYTES, LLP_ERR_UNSUPPORTED,
+            "the request needs %zu bytes of forward workspace; the static scratch holds %zu "
+            "(use llp_forward with a caller workspace, or fewer rows per call)", need,
+            SCRATCH_BYTES);
+  st = check_device();
+  if (st != LLP_OK) return st;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(LLP_ERR_HIP, "hipGetDevice failed");
+  void* ws = scratch_address(dev);
+  LLP_CHECK(ws != nullptr, LLP_ERR_INTERNAL, "static scratch not set up on device %d", dev);
+  return forward_impl(req, out, ws, SCRATCH_BYTES, stream);
 }
 
 LLP_API llp_status llp_merge(int32_t world, const llp_partials* parts, int64_t num_tokens,

@@ -13,6 +13,10 @@ namespace llp {
 // row's summation order never depends on the batch.
 constexpr int DH_SPLITS = 2;
 constexpr int TILE = 256;  // BM = BN of every GEMM tile
+// Static device scratch of llp_forward_noalloc: the forward workspace of up to this many bytes
+// (T = 4096 rows over a 151936-column vocabulary need 29.2 MB).
+constexpr size_t SCRATCH_BYTES = size_t(32) << 20;
+constexpr int MAX_DEVICES = 64;
 constexpr int KSTEP = 64;  // K depth of one pipelined GEMM step
 
 struct LayoutArgs {
@@ -246,5 +250,10 @@ hipError_t launch_zero_rows(const ZeroArgs& a, hipStream_t s);
 hipError_t launch_logits(const LogitsArgs& a, hipStream_t s);
 hipError_t launch_keep(const KeepArgs& a, hipStream_t s);
 hipError_t probe_kernels();
+// Looks up this device's copy of the static scratch (the current device must be `device`);
+// idempotent. Called under the library's open lock.
+hipError_t scratch_init(int device);
+// The device address of that copy, or null before scratch_init succeeded on the device.
+void* scratch_address(int device);
 
 }  // namespace llp

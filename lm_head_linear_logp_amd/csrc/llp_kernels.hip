@@ -1367,6 +1367,32 @@ hipError_t launch_keep(const KeepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------
+// Static scratch for llp_forward_noalloc, the forward for callers that cannot allocate device
+// memory. The array is part of the code object, so every device the library is loaded on
+// holds its own copy (SCRATCH_BYTES each, until the process ends) at its own address. In host
+// code `scratch` names a host-side stand-in, not device memory: the device address is looked
+// up once per device with hipGetSymbolAddress (scratch_init, called by llp_open with that
+// device current) and only that address is handed to kernels.
+// ------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+static void* g_scratch_addr[MAX_DEVICES];
+
+hipError_t scratch_init(int device) {
+  if (device < 0 || device >= MAX_DEVICES) return hipErrorInvalidDevice;
+  if (g_scratch_addr[device] != nullptr) return hipSuccess;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (p == nullptr) return hipErrorInvalidSymbol;
+  g_scratch_addr[device] = p;
+  return hipSuccess;
+}
+
+void* scratch_address(int device) {
+  return device >= 0 && device < MAX_DEVICES ? g_scratch_addr[device] : nullptr;
+}
+
 hipError_t probe_kernels() {
   hipFuncAttributes attr;
   return hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(k_fwd<BIAS_NONE, FWD_WAVES>));
