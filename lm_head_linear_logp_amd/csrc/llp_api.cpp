@@ -121,7 +121,7 @@ llp_status check_request(const llp_request* req) {
 
 // Workspace regions (byte offsets, each 256-byte aligned).
 struct Ws {
-  size_t count, scored, pos, tloc, tz, pm, ps, pq, G, hgT, P, total;
+  size_t count, qctr, scored, pos, tloc, tz, pm, ps, pq, G, hgT, P, total;
   int64_t T_cap, nvt, ldg;
 };
 
@@ -137,6 +137,7 @@ Ws ws_layout(int64_t T, int64_t n_real, int64_t H, int op) {
     return o;
   };
   w.count = take(256);
+  w.qctr = take(256);   // tile-queue counters: QCTR_INTS per GEMM kernel of the call
   w.scored = take((size_t)w.T_cap * 4);
   w.pos = take((size_t)w.T_cap * 4);
   w.tloc = take((size_t)w.T_cap * 4);
@@ -589,6 +590,9 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
   la.pos = at<int32_t>(workspace, w.pos);
   la.tloc = at<int32_t>(workspace, w.tloc);
   la.status = req->status_word;
+  int32_t* qctr = at<int32_t>(workspace, w.qctr);   // gradient, dhidden, dweight counters
+  la.qctr = qctr;
+  la.nqctr = 3 * QCTR_INTS;
   LLP_HIP(launch_layout(la, s), "layout kernel launch");
 
   const int ntb = (int)(w.T_cap / TILE);
@@ -629,7 +633,8 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
     ga.ent = in->entropy;
     ga.G = G;
     ga.ldg = w.ldg;
-    LLP_HIP(launch_grad(ga, s), "gradient kernel launch");
+    ga.qctr = qctr;
+      LLP_HIP(launch_grad(ga, s), "gradient kernel launch");
 
     DhArgs da{};
     da.G = G;
@@ -645,7 +650,8 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
     da.count = la.count;
     da.P = P;
     da.pstride = w.T_cap;
-    LLP_HIP(launch_dh(da, s), "dhidden kernel launch");
+    da.qctr = qctr + QCTR_INTS;
+      LLP_HIP(launch_dh(da, s), "dhidden kernel launch");
 
     DwArgs wa{};
     wa.G = G;
@@ -660,7 +666,8 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
     wa.dW = out->dweight;
     wa.lddw = out->dweight_stride;
     wa.overwrite = overwrite;
-    LLP_HIP(launch_dw(wa, s), "dweight kernel launch");
+    wa.qctr = qctr + 2 * QCTR_INTS;
+      LLP_HIP(launch_dw(wa, s), "dweight kernel launch");
 
     if (out->dbias != nullptr) {
       DbArgs ba{};

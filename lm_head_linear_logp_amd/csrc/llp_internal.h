@@ -18,6 +18,7 @@ constexpr int TILE = 256;  // BM = BN of every GEMM tile
 constexpr size_t SCRATCH_BYTES = size_t(32) << 20;
 constexpr int MAX_DEVICES = 64;
 constexpr int KSTEP = 64;  // K depth of one pipelined GEMM step
+constexpr int QCTR_INTS = 16;  // tile-queue counters per GEMM kernel launch (llp_tile.hpp)
 
 struct LayoutArgs {
   int64_t T;
@@ -37,6 +38,8 @@ struct LayoutArgs {
   float* out_e;
   float* out_p;
   int32_t* status;
+  int32_t* qctr;    // tile-queue counters of the GEMM kernels of this call, zeroed here
+  int32_t nqctr;    // (at most 1024)
 };
 
 struct FwdArgs {
@@ -168,6 +171,7 @@ struct GradArgs {
   const float* ent;
   uint16_t* G;
   int64_t ldg;
+  int32_t* qctr;    // tile-queue counters (QCTR_INTS), zero at launch
 };
 
 struct DhArgs {
@@ -181,6 +185,7 @@ struct DhArgs {
   const int32_t* count;
   float* P;
   int64_t pstride;  // rows per split
+  int32_t* qctr;    // tile-queue counters (QCTR_INTS), zero at launch
 };
 
 struct DhReduceArgs {
@@ -206,6 +211,7 @@ struct DwArgs {
   float* dW;
   int64_t lddw;
   int32_t overwrite;  // 1: dW = the product (no read of dW); 0: dW += the product
+  int32_t* qctr;    // tile-queue counters (QCTR_INTS), zero at launch
 };
 
 struct ZeroArgs {

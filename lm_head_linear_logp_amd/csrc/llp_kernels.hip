@@ -26,6 +26,8 @@ __global__ __launch_bounds__(1024) void k_layout(LayoutArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int status = 0;
   if (tid == 0) carry_s = 0;
+  // The tile-queue counters of the GEMM kernels that follow on this stream start at 0.
+  if (tid < a.nqctr) a.qctr[tid] = 0;
   __syncthreads();
   for (int64_t base = 0; base < a.T; base += 1024) {
     const int64_t t = base + tid;
@@ -282,6 +284,7 @@ __device__ __forceinline__ void weight_hidden_loaders(const uint16_t* W, int64_t
 // The epilogue reuses the pipeline's LDS for 6 x 256 fp32 partials.
 static_assert(6 * 256 * 4 <= dma::LDS_BYTES, "forward epilogue LDS");
 static_assert(dma::BKD == KSTEP, "K step shared with the host");
+static_assert(QCTR_INTS > NUM_XCD, "queue counters and the all-empty flag");
 
 // One kernel per bias mode, differing only in how the accumulators start: a run-time choice
 // there makes the compiler spill accumulators in the epilogue.
@@ -295,6 +298,9 @@ template <int BMODE, int NW>
 __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_fwd(FwdArgs a) {
   constexpr int NFB = 16 / NW;
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
+  // One workgroup per tile in the static XCD order: the forward's tiles are not drawn from
+  // the tile queues. Under the chip's power limit the queues' dynamic tail (its atomics and
+  // surplus workgroups) cost the forward ~5% while they saved the backward kernels ~2%.
   int vt, tb;
   vocab_token_tile(xcd_remap(blockIdx.x, gridDim.x), a.nvt, a.ntb, vt, tb);
   const int Ts = *a.count;
@@ -741,8 +747,10 @@ template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_grad(GradArgs a) {
   constexpr int NFB = 16 / NW;
   __shared__ __attribute__((aligned(16))) uint16_t smem[BWDG_LDS_BYTES / 2];
+  const int tile = take_tile(a.qctr, a.nvt * a.ntb, reinterpret_cast<int*>(smem));
+  if (tile < 0) return;
   int vt, tb;
-  vocab_token_tile(xcd_remap(blockIdx.x, gridDim.x), a.nvt, a.ntb, vt, tb);
+  vocab_token_tile(tile, a.nvt, a.ntb, vt, tb);
   const int Ts = *a.count;
   const int j0 = tb * BN, v0 = vt * BM;
   if (j0 >= Ts) return;
@@ -773,8 +781,9 @@ template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_dh(DhArgs a) {
   constexpr int NFB = 16 / NW;
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int per = a.ntm * a.ntn;
+  const int tile = take_tile(a.qctr, per * a.nsplit, reinterpret_cast<int*>(smem));
+  if (tile < 0) return;
   const int sp = tile / per;
   int mt, nt;
   vocab_token_tile(tile % per, a.ntm, a.ntn, mt, nt);
@@ -926,10 +935,12 @@ __device__ __forceinline__ void dw_store(const f32x16 (&acc)[4][4], const DwTile
 template <bool OVERWRITE>
 __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_dw(DwArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
-  int mt, nt;
-  vocab_token_tile<4>(xcd_remap(blockIdx.x, gridDim.x), a.ntm, a.ntn, mt, nt);
+  const int tile = take_tile(a.qctr, a.ntm * a.ntn, reinterpret_cast<int*>(smem));
+  if (tile < 0) return;
   const int Ts = *a.count;
   if (!OVERWRITE && Ts <= 0) return;
+  int mt, nt;
+  vocab_token_tile<4>(tile, a.ntm, a.ntn, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
   DwTile t;
   dw_tile_setup(a, m0, n0, t);
@@ -1281,6 +1292,12 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The GEMM grids: OVERSUBSCRIBE workgroups per tile, each drawing its tile from the per-XCD
+// queues whose counters the layout kernel zeroed.
+static inline unsigned workers(int tiles) {
+  return (unsigned)(((int64_t)tiles * OVERSUBSCRIBE_NUM + OVERSUBSCRIBE_DEN - 1) / OVERSUBSCRIBE_DEN);
+}
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   if (a.nvt > 0 && a.ntb > 0) {
     const dim3 grid(a.nvt * a.ntb), block(64 * FWD_WAVES);
@@ -1310,13 +1327,15 @@ hipError_t launch_topp(const ToppArgs& a, hipStream_t s) {
 
 hipError_t launch_grad(const GradArgs& a, hipStream_t s) {
   if (a.nvt > 0 && a.ntb > 0)
-    hipLaunchKernelGGL(k_grad<GRAD_WAVES>, dim3(a.nvt * a.ntb), dim3(64 * GRAD_WAVES), 0, s, a);
+    hipLaunchKernelGGL(k_grad<GRAD_WAVES>, dim3(workers(a.nvt * a.ntb)),
+                       dim3(64 * GRAD_WAVES), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dh(const DhArgs& a, hipStream_t s) {
   const int n = a.ntm * a.ntn * a.nsplit;
-  if (n > 0) hipLaunchKernelGGL(k_dh<DH_WAVES>, dim3(n), dim3(64 * DH_WAVES), 0, s, a);
+  if (n > 0)
+    hipLaunchKernelGGL(k_dh<DH_WAVES>, dim3(workers(n)), dim3(64 * DH_WAVES), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1329,8 +1348,9 @@ hipError_t launch_dh_reduce(const DhReduceArgs& a, hipStream_t s) {
 hipError_t launch_dw(const DwArgs& a, hipStream_t s) {
   const int n = a.ntm * a.ntn;
   if (n > 0) {
-    if (a.overwrite) hipLaunchKernelGGL(k_dw<true>, dim3(n), dim3(NTHREADS), 0, s, a);
-    else hipLaunchKernelGGL(k_dw<false>, dim3(n), dim3(NTHREADS), 0, s, a);
+    const dim3 grid(workers(n));
+    if (a.overwrite) hipLaunchKernelGGL(k_dw<true>, grid, dim3(NTHREADS), 0, s, a);
+    else hipLaunchKernelGGL(k_dw<false>, grid, dim3(NTHREADS), 0, s, a);
   }
   return hipGetLastError();
 }

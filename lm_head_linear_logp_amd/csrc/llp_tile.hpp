@@ -44,6 +44,65 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return x * full + (x < rem ? x : rem) + i;
 }
 
+// Work distribution over the XCDs for the backward GEMM kernels. The XCDs of one chip run at
+// different clocks under load (measured 1.60-1.80 GHz within one launch), so equal shares of
+// tiles per XCD leave the fast ones idle while the slowest finishes. Hardware dispatch puts
+// workgroup b on XCD b % 8 and each XCD starts its share of the grid in order (b / 8) as its
+// CUs free up. XCD x owns the contiguous range of logical tiles xcd_remap gives it (its
+// queue), so the CUs of an XCD run consecutive tiles that share operand slices in its L2. The
+// first 3/4 of a queue go to the XCD's workgroups by position, with no synchronisation; the
+// last quarter is handed out in order through a counter, to the XCD's later workgroups and,
+// once it runs dry, to other XCDs' workgroups that have emptied their own. The grid holds
+// OVERSUBSCRIBE workgroups per tile, so a faster XCD runs more workgroups and so more tiles; a
+// workgroup that finds every queue empty exits. Which workgroup runs a tile changes nothing in
+// that tile's arithmetic: results are bitwise those of any other assignment. (The forward
+// keeps one workgroup per tile in the static order: there the dynamic tail measured ~5%
+// slower, the backward kernels ~2% faster.)
+constexpr int OVERSUBSCRIBE_NUM = 5, OVERSUBSCRIBE_DEN = 4;   // workgroups per tile: 1.25
+// A launch's counters (QCTR_INTS of them, llp_internal.h): [0, 8) the queues' dynamic parts,
+// [8] set once every queue is empty.
+
+__device__ __forceinline__ int queue_first(int n, int x) {
+  const int full = n / NUM_XCD, rem = n % NUM_XCD;
+  return x * full + (x < rem ? x : rem);
+}
+__device__ __forceinline__ int queue_size(int n, int x) {
+  return n / NUM_XCD + (x < n % NUM_XCD ? 1 : 0);
+}
+__device__ __forceinline__ int queue_static(int size) { return size - (size + 3) / 4; }
+
+// The workgroup's logical tile of n, or -1 when every queue is empty. Called by every thread
+// (the static branch is uniform). For a dynamic tile, thread 0 takes it with global atomic
+// operations (vector memory) on ctr[0..8] (zero at the launch), own XCD's queue first, and the
+// tile reaches the other threads through `slot`, a word of the pipeline's LDS (a separate
+// __shared__ word would take the workgroup past 128 KiB of LDS: for the 8-wave forward tile
+// 4 more bytes measured 62% slower).
+__device__ __forceinline__ int take_tile(int* ctr, int n, int* slot) {
+  const int x = blockIdx.x % NUM_XCD, i = blockIdx.x / NUM_XCD;
+  const int s0 = queue_static(queue_size(n, x));
+  if (i < s0) return queue_first(n, x) + i;
+  if (threadIdx.x == 0) {
+    int t = -1;
+    int k = atomicAdd(ctr + x, 1);
+    if (k < queue_size(n, x) - s0) {
+      t = queue_first(n, x) + s0 + k;
+    } else if (atomicOr(ctr + NUM_XCD, 0) == 0) {
+      for (int d = 1; d < NUM_XCD && t < 0; ++d) {
+        const int y = (x + d) % NUM_XCD;
+        const int sy = queue_static(queue_size(n, y));
+        k = atomicAdd(ctr + y, 1);
+        if (k < queue_size(n, y) - sy) t = queue_first(n, y) + sy + k;
+      }
+      if (t < 0) atomicOr(ctr + NUM_XCD, 1);
+    }
+    *slot = t;
+  }
+  __syncthreads();
+  const int t = *slot;
+  __syncthreads();   // the slot sits in the pipeline's LDS, which the first DMA overwrites
+  return t;
+}
+
 // Logical tile -> (vocabulary tile, token block) for the vocabulary x token grids. Tiles
 // run in groups of VG vocabulary tiles x all token blocks, token block slowest within a group:
 // with VG = 8 the 32 workgroups an XCD runs at once cover 8 vocabulary tiles x 4 token blocks,
