@@ -108,30 +108,152 @@ def ingest_pmc(fetch_csv: str, write_csv: str) -> None:
     print(json.dumps(out, indent=1))
 
 
-def cpu_baseline(rows: int = 2560) -> dict:
-    """The fp64 oracle (as it stands) on `rows` rows of the same workload: forward + backward
-    of each row, timed on this host's cores; scaled to scored tokens/s."""
-    import oracle
-    import synth
+def host_cpu() -> dict:
+    """The host the CPU baseline runs on: CPU model, logical CPUs, CPUs this process may use,
+    and the BLAS thread count the oracle's matrix products get."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
     except Exception:
-        threads = os.cpu_count()
+        blas = os.cpu_count()
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable,
+            "blas_threads": int(blas), "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def cpu_baseline(rows: int = 2560) -> dict:
+    """The fp64 oracle (as it stands) timed on this host's cores, excluding input generation
+    and conversion:
+      * the bench workload: forward + backward of `rows` of the 4096 config-2 rows (the
+        reported value, scaled to scored tokens/s);
+      * config 1 (T=64, H=256, V=1000/1024): forward, 1 warm-up + 5 reps, in ms;
+      * config 5 (top-p replay of 4096 rows over 4 shards and the merge): 1 rep, in s;
+      * config 4 (16 packed sequences, 40874 scored rows, forward + backward): stated from the
+        measured per-row forward+backward rate, which it shares (the same products per row;
+        the per-chunk dweight product is part of that rate), not run (it would take minutes)."""
+    import oracle
+    import synth
+    hc = host_cpu()
     base = synth.config2_base()
     tg = np.loadtxt(os.path.join(ROOT, "tests", "golden", "config2_targets.txt"), dtype=np.int64,
                     comments="#")
     w64 = oracle.bf16_to_f64(synth.full_weight()[:VR])   # input conversion, not timed
     h = base["hidden"][:rows]
     dlogp = synth.rng(2, 70).standard_normal(rows)
+    log(f"cpu baseline: oracle forward+backward of {rows} rows")
     t0 = time.perf_counter()
     f = oracle.forward(h, w64, None, TAU, tg[:rows], None, VR)
     oracle.backward(h, w64, None, TAU, tg[:rows], None, 0, VP, VR, f["lse"], dlogp)
     dt = time.perf_counter() - t0
-    return {"value": rows / dt, "unit": "scored tokens/s", "cores": int(threads),
-            "kind": "oracle",
+    del w64
+    c1 = synth.config1()
+    c1w = oracle.bf16_to_f64(c1["weight"])
+    reps = []
+    for i in range(6):
+        t1 = time.perf_counter()
+        oracle.forward(c1["hidden"], c1w, c1["bias"], c1["temperature"], c1["targets"],
+                       c1["mask"], c1["real_vocab"])
+        if i:
+            reps.append((time.perf_counter() - t1) * 1e3)
+    log("cpu baseline: oracle top-p replay of config 5")
+    tp = synth.topp_case()
+    t1 = time.perf_counter()
+    parts = []
+    for off, n in synth.shard_ranges():
+        p = oracle.top_p_replay(tp["logits"][:, off:off + n], tp["replay_ids"], tp["targets"],
+                                TAU, off, n, VR)
+        p["entropy"] = None
+        parts.append(p)
+    oracle.merge(parts)
+    c5 = time.perf_counter() - t1
+    c4_scored = int(synth.config4_layout()["mask"].sum())
+    rate = rows / dt
+    return {"value": rate, "unit": "scored tokens/s", "cores": hc["blas_threads"],
+            "kind": "oracle", "host": hc,
             "sample": f"fp64 oracle forward+backward of {rows} of the 4096 rows "
-                      f"(H=4096, V=151669/151936), {dt:.1f} s on {threads} BLAS threads"}
+                      f"(H=4096, V=151669/151936), {dt:.1f} s on {hc['blas_threads']} BLAS "
+                      f"threads",
+            "config1_forward_ms": {"median": float(np.median(reps)), "min": float(min(reps)),
+                                   "reps": len(reps)},
+            "config5_topp_4shards_merge_s": c5,
+            "config4_forward_backward_s_stated": {
+                "value": c4_scored / rate, "scored_rows": c4_scored,
+                "how": "scored rows / the measured forward+backward rate (not run)"}}
+
+
+def gpu_clock_sampler(device_index: int = 0):
+    """Samples the GPU's graphics clock (amdsmi) in a background thread while the timed steps
+    run. Returns (start, stop) callables; stop() gives a summary dict, or None with a reason
+    when no sample could be taken."""
+    import threading
+    state = {"samples": [], "error": None}
+    stop_ev = threading.Event()
+
+    def pick_handle(amdsmi):
+        import torch
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if len(handles) == 1:
+            return handles[0]
+        pr = torch.cuda.get_device_properties(device_index)
+        bus = getattr(pr, "pci_bus_id", None)
+        for h in handles:
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)     # "dddd:bb:dd.f"
+            if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                return h
+        return handles[0]
+
+    def run():
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            try:
+                h = pick_handle(amdsmi)
+                while not stop_ev.is_set():
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                    cur = m.get("current_gfxclks")
+                    vals = [v for v in (cur if isinstance(cur, (list, tuple)) else [cur])
+                            if isinstance(v, (int, float)) and 0 < v < 10000]
+                    if not vals:
+                        v = m.get("average_gfxclk_frequency")
+                        vals = [v] if isinstance(v, (int, float)) and 0 < v < 10000 else []
+                    if vals:
+                        state["samples"].append(tuple(float(v) for v in vals))
+                    stop_ev.wait(0.01)
+            finally:
+                amdsmi.amdsmi_shut_down()
+        except Exception as e:  # no amdsmi, no permission, unknown metrics layout
+            state["error"] = f"{type(e).__name__}: {e}"
+
+    th = threading.Thread(target=run, daemon=True)
+
+    def stop():
+        stop_ev.set()
+        th.join(timeout=5)
+        xs = state["samples"]
+        if not xs:
+            return {"mhz_median": None, "reason": state["error"] or "no samples"}
+        mean = np.array([np.mean(x) for x in xs])
+        per = [np.median([x[i] for x in xs if len(x) > i]) for i in range(max(len(x) for x in xs))]
+        return {"mhz_median": float(np.median(mean)), "mhz_min": float(mean.min()),
+                "mhz_max": float(mean.max()), "samples": len(xs),
+                "distinct_samples": len(set(xs)),
+                "per_xcd_mhz_median": [float(v) for v in per],
+                "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), sampled every "
+                          "10 ms from the warm-up to the end of the timed steps; the firmware "
+                          "refreshes these values less often than that (distinct_samples)"}
+    return th.start, stop
 
 
 def measure_vendor_gemm(h, W, stream, reps=10):
@@ -369,6 +491,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    clk_start, clk_stop = gpu_clock_sampler(0)
+    clk_start()
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step(False)
@@ -380,7 +504,9 @@ def main():
         events.append(step(True))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock = clk_stop()
     ph = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events])  # ms
+    per_step = np.array([e[0].elapsed_time(e[4]) for e in events])                    # ms
     total_ms = float(events[0][0].elapsed_time(events[-1][4]))
     ms_per_step = total_ms / args.steps
     fwd_ms, merge_ms, bwd_ms, topp_ms = (float(x) for x in ph.mean(axis=0))
@@ -429,8 +555,15 @@ def main():
                      "bound": "mfma", "achieved": ach_fwd, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": ach_fwd / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic()},
+        "ms_per_step_median": float(np.median(per_step)),
+        "ms_per_step_min": float(per_step.min()),
+        "gpu_clock": clock,
         "phases_ms": {"forward": fwd_ms, "merge": merge_ms, "backward": bwd_ms,
                       "top_p_4shards_plus_merge": topp_ms},
+        "phases_ms_median": {k: float(v) for k, v in zip(
+            ("forward", "merge", "backward", "top_p_4shards_plus_merge"), np.median(ph, axis=0))},
+        "phases_ms_min": {k: float(v) for k, v in zip(
+            ("forward", "merge", "backward", "top_p_4shards_plus_merge"), ph.min(axis=0))},
         "forward_tokens_per_s": T / (fwd_ms * 1e-3),
         "backward_tflops": ach_bwd,
         "backward_accumulate": {"ms": bwd_acc_ms, "tflops": flop_bwd / (bwd_acc_ms * 1e-3) / 1e12,
