@@ -55,7 +55,9 @@ llp_status check_partition(const llp_vocab_partition& v) {
   LLP_CHECK(v.real_vocab > 0 && v.real_vocab <= v.padded_vocab, LLP_ERR_INVALID_ARGUMENT,
             "need 0 < real_vocab (%lld) <= padded_vocab (%lld)", (long long)v.real_vocab,
             (long long)v.padded_vocab);
-  LLP_CHECK(v.offset >= 0 && v.local_size >= 0 && v.offset + v.local_size <= v.padded_vocab,
+  // Compared without forming offset + local_size, which could overflow.
+  LLP_CHECK(v.offset >= 0 && v.local_size >= 0 && v.offset <= v.padded_vocab &&
+                v.local_size <= v.padded_vocab - v.offset,
             LLP_ERR_INVALID_ARGUMENT, "shard [offset=%lld, +local_size=%lld) outside padded vocab %lld",
             (long long)v.offset, (long long)v.local_size, (long long)v.padded_vocab);
   if (v.world == 1)

@@ -416,3 +416,12 @@ def test_keep_mask_replay_rejects_entropy_output():
     r = good_keep_request()
     o = A.llp_partials(FAKE, FAKE, FAKE, FAKE, FAKE)
     assert A.load().llp_keep_mask_replay(C.byref(r), C.byref(o), None) == A.LLP_ERR_INVALID_ARGUMENT
+
+
+def test_partition_offset_near_int64_max_is_refused():
+    """offset + local_size past the int64 range is refused, not overflowed."""
+    r = good_request()
+    r.vocab.world, r.vocab.offset, r.vocab.local_size = 2, (1 << 63) - 6, 100
+    n = C.c_size_t()
+    assert A.load().llp_workspace_bytes(C.byref(r), A.LLP_OP_FORWARD, C.byref(n)) == \
+        A.LLP_ERR_INVALID_ARGUMENT
