@@ -133,7 +133,7 @@ def host_cpu() -> dict:
             "blas_threads": int(blas), "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
-def cpu_baseline(rows: int = 2560) -> dict:
+def cpu_baseline(rows: int = 2560, topp: dict = None) -> dict:
     """The fp64 oracle (as it stands) timed on this host's cores, excluding input generation
     and conversion:
       * the bench workload: forward + backward of `rows` of the 4096 config-2 rows (the
@@ -168,7 +168,7 @@ def cpu_baseline(rows: int = 2560) -> dict:
         if i:
             reps.append((time.perf_counter() - t1) * 1e3)
     log("cpu baseline: oracle top-p replay of config 5")
-    tp = synth.topp_case()
+    tp = topp if topp is not None else synth.topp_case()
     t1 = time.perf_counter()
     parts = []
     for off, n in synth.shard_ranges():
@@ -388,25 +388,56 @@ def measure_config4(llp, W, stream, busy, reps=2):
                          loss_mask=mk[c0:c1], real_vocab=VR, padded_vocab=VP, dweight=dW,
                          dhidden=dH[c0:c1], overwrite=(i == 0))
 
-    one_pass()
-    torch.cuda.synchronize()
-    busy()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(reps):
-        one_pass()
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
+    lse = torch.empty(Tp, dtype=torch.float32, device="cuda")
+    ws = {}
+
+    def one_pass_whole():
+        # The forward in chunks of 4096 rows as above; then ONE backward over the whole pack
+        # with the chunks' lse: dweight is written once (no read-modify-write per chunk).
+        for c0, c1 in chunks:
+            o = llp.forward(h[c0:c1], W, tg[c0:c1], temperature=TAU, loss_mask=mk[c0:c1],
+                            real_vocab=VR, padded_vocab=VP, want_entropy=False)
+            lse[c0:c1] = o["lse"]
+        llp.backward(h, W, tg, lse, dl, temperature=TAU, loss_mask=mk, real_vocab=VR,
+                     padded_vocab=VP, dweight=dW, dhidden=dH, overwrite=True,
+                     workspace=ws.get("bwd"))
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        busy()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    ms = timed(one_pass)
+    # The whole-pack backward's workspace (G for every scored row: ~17 GB here), allocated
+    # once outside the timed passes, as a training loop would keep it.
+    import lm_head_linear_logp_amd._capi as capi
+    req = llp._request(h, W, tg, TAU, None, mk, None, 0, VR, VP, 0, 1, False, None)
+    ws["bwd"] = torch.empty(llp.workspace_bytes(req, capi.LLP_OP_BACKWARD), dtype=torch.uint8,
+                            device="cuda")
+    ms_whole = timed(one_pass_whole)
     flop = 4.0 * 2.0 * H * VR * scored   # forward + the backward's three products
-    del h, tg, mk, dl, dH, dW
+    ws_gb = ws["bwd"].numel() / 1e9
+    del h, tg, mk, dl, dH, dW, lse, ws
     torch.cuda.empty_cache()
     return {"config4_forward_backward": {
         "packed_tokens": Tp, "scored_tokens": scored, "chunks": len(chunks), "ms": ms,
         "scored_tokens_per_s": scored / (ms * 1e-3), "tflops": flop / (ms * 1e-3) / 1e12,
         "workload": "16 packed sequences, lengths U{256..7168}, first 20-40% of each masked, "
                     "chunks of 4096 rows in order; forward then backward per chunk, dweight "
-                    "overwritten by the first chunk and accumulated by the rest"}}
+                    "overwritten by the first chunk and accumulated by the rest"},
+        "config4_forward_chunked_backward_whole": {
+            "ms": ms_whole, "scored_tokens_per_s": scored / (ms_whole * 1e-3),
+            "tflops": flop / (ms_whole * 1e-3) / 1e12, "backward_workspace_GB": ws_gb,
+            "workload": "the same pass: forward per 4096-row chunk, then one backward over "
+                        "all 56583 rows (dweight written once; logp and dhidden rows bitwise "
+                        "those of the chunked pass, dweight equal to rounding)"}}
 
 
 def main():
@@ -460,7 +491,9 @@ def main():
     logits = torch.from_numpy(tp["logits"]).cuda()
     rids = torch.from_numpy(tp["replay_ids"]).cuda()
     rtg = torch.from_numpy(tp["targets"]).cuda()
-    del tp
+    if args.no_cpu_baseline:
+        del tp
+        tp = None
     shards = synth.shard_ranges()
     dW = torch.empty((VP, H), dtype=torch.float32, device="cuda")
     dH = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
@@ -585,7 +618,7 @@ def main():
         log(f"cpu baseline: oracle on {args.cpu_rows} rows")
         del W, h, logits, dW, dH
         torch.cuda.empty_cache()
-        res["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+        res["cpu_baseline"] = cpu_baseline(args.cpu_rows, tp)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -14,14 +14,16 @@
 namespace llp {
 
 // ------------------------------------------------------------------------------------
-// Layout and mask indexing. One workgroup scans the loss mask in order and writes the
-// compact list of scored rows, each row's compact index (-1 when unscored), the target's
-// local column (-1 when outside this shard's real columns), zero outputs for unscored rows,
-// and status bits ([CUDA provider, "Summary"]: the framework keeps token layout and
+// Layout and mask indexing. One workgroup scans the loss mask in order (16 rows per thread and
+// pass) and writes the compact list of scored rows, each row's compact index (-1 when
+// unscored), the target's local column (-1 when outside this shard's real columns), zero
+// outputs for unscored rows, and status bits ([CUDA provider, "Summary"]: the framework keeps token layout and
 // masking; the operator scores unmasked rows only).
 // ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_layout(LayoutArgs a) {
-  __shared__ int wsum[16];
+constexpr int LAYOUT_THREADS = 1024, LAYOUT_ROWS = 16;   // rows per thread per pass
+
+__global__ __launch_bounds__(LAYOUT_THREADS) void k_layout(LayoutArgs a) {
+  __shared__ int wsum[LAYOUT_THREADS / 64];
   __shared__ int carry_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int status = 0;
@@ -29,19 +31,35 @@ __global__ __launch_bounds__(1024) void k_layout(LayoutArgs a) {
   // The tile-queue counters of the GEMM kernels that follow on this stream start at 0.
   if (tid < a.nqctr) a.qctr[tid] = 0;
   __syncthreads();
-  for (int64_t base = 0; base < a.T; base += 1024) {
-    const int64_t t = base + tid;
-    const bool in = t < a.T;
-    const bool sc = in && (a.mask == nullptr || a.mask[t] != 0);
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(sc);
-    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-    if (lane == 0) wsum[wave] = __popcll(bal);
+  // Each pass covers LAYOUT_THREADS * LAYOUT_ROWS rows; thread tid takes LAYOUT_ROWS
+  // consecutive ones. Its scored rows get consecutive compact indices after those of all
+  // lower threads (an exclusive scan of the per-thread counts), so the compaction keeps row
+  // order, as a serial scan would.
+  for (int64_t base = 0; base < a.T; base += (int64_t)LAYOUT_THREADS * LAYOUT_ROWS) {
+    const int64_t t0 = base + (int64_t)tid * LAYOUT_ROWS;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int k = 0; k < LAYOUT_ROWS; ++k) {
+      const int64_t t = t0 + k;
+      if (t < a.T && (a.mask == nullptr || a.mask[t] != 0)) bits |= 1u << k;
+    }
+    const int cnt = __popc(bits);
+    int incl = cnt;  // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     int pre = carry_s;
     for (int w = 0; w < wave; ++w) pre += wsum[w];
-    const int j = pre + below;
-    if (in) {
+    int j = pre + incl - cnt;
+#pragma unroll
+    for (int k = 0; k < LAYOUT_ROWS; ++k) {
+      const int64_t t = t0 + k;
+      if (t >= a.T) continue;
+      const bool sc = (bits >> k) & 1u;
       a.pos[t] = sc ? j : -1;
       if (sc) {
         a.scored[j] = (int)t;
@@ -52,6 +70,7 @@ __global__ __launch_bounds__(1024) void k_layout(LayoutArgs a) {
         const bool hit = valid && loc >= 0 && loc < a.n_real;
         a.tloc[j] = hit ? (int)loc : -1;
         if (!hit && a.world == 1) status |= LLP_STATUS_TARGET_NOT_FOUND;
+        ++j;
       } else {
         if (a.out_t) a.out_t[t] = 0.f;
         if (a.out_f) a.out_f[t] = 0;
@@ -63,14 +82,14 @@ __global__ __launch_bounds__(1024) void k_layout(LayoutArgs a) {
     __syncthreads();
     if (tid == 0) {
       int tot = 0;
-      for (int w = 0; w < 16; ++w) tot += wsum[w];
+      for (int w = 0; w < LAYOUT_THREADS / 64; ++w) tot += wsum[w];
       carry_s += tot;
     }
     __syncthreads();
   }
   if (tid == 0) a.count[0] = carry_s;
   if (a.cu_seqlens != nullptr) {
-    for (int i = tid; i <= a.num_seqs; i += 1024) {
+    for (int i = tid; i <= a.num_seqs; i += LAYOUT_THREADS) {
       const int c = a.cu_seqlens[i];
       if (i == 0 && c != 0) status |= LLP_STATUS_LAYOUT_INVALID;
       if (i == a.num_seqs && (int64_t)c != a.T) status |= LLP_STATUS_LAYOUT_INVALID;
@@ -1288,7 +1307,7 @@ __global__ __launch_bounds__(256) void k_keep(KeepArgs a) {
 }
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_layout, dim3(1), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(k_layout, dim3(1), dim3(LAYOUT_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

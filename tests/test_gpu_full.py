@@ -7,7 +7,9 @@ Every row is compared with the fp64 oracle on the same seeded inputs:
     dhidden on two whole chunks plus a seeded 512-row sample of the others, and the dweight
     accumulated over all 14 chunks on a vocabulary subset holding every target, the
     real/padded boundary and 2048 seeded other rows; the repack (shuffled sequences, chunks of
-    3000) is bitwise per row for logp and dhidden, and dweight is bitwise run to run;
+    3000) is bitwise per row for logp and dhidden, and dweight is bitwise run to run; one
+    backward call over the whole pack gives the chunked dhidden bitwise and its dweight to
+    rounding;
   * config 5: the top-p replay of all rows, unsharded, per shard and merged.
 Observed errors are printed (and logged when LLP_PARITY_LOG is set) and held to regression
 guards far below the parity bounds.
@@ -201,6 +203,14 @@ def config4(llp, weight):
     torch.cuda.synchronize()
     same_dw = bytes_equal(dW, dW2) and bytes_equal(dH, dH2)
     del dH2, dW2
+    # One backward call over the whole pack (T = 56583; G for all scored rows, ~17 GB).
+    whole = run_backward_chunks(llp, W, hd, tg, mk, dl, lse, T)
+    torch.cuda.synchronize()
+    whole_dH_same = bytes_equal(whole[0], dH)
+    whole_dW_rel = normwise_rel(host(whole[1])[:VR], host(dW)[:VR])
+    whole_dW_pad = bool(np.all(host(whole[1])[VR:] == 0))
+    del whole
+    torch.cuda.empty_cache()
     idx = repack_index(synth.repack_order(), case["lens"])
     ix = dev(idx)
     logp_b, lse_b = run_forward_chunks(llp, W, hd[ix], tg[ix], mk[ix], 3000)
@@ -208,7 +218,8 @@ def config4(llp, weight):
     torch.cuda.synchronize()
     out = dict(case=case, idx=idx, logp=host(logp), lse=host(lse), dH=host(dH),
                dW=host(dW), same_dw=same_dw, logp_b=host(logp_b), dH_b=host(dH_b),
-               dW_b=host(dW_b))
+               dW_b=host(dW_b), whole_dH_same=whole_dH_same, whole_dW_rel=whole_dW_rel,
+               whole_dW_pad=whole_dW_pad)
     del hd, dW, dW_b, dH, dH_b
     torch.cuda.empty_cache()
     return out
@@ -244,6 +255,16 @@ def test_config4_repack_bitwise(config4):
     record("config4 dweight repacked vs chunked (normwise)", r)
     assert r <= 1e-5
     assert config4["same_dw"], "dweight / dhidden differ between two runs of the same chunks"
+
+
+def test_config4_whole_pack_backward(config4):
+    """One backward call over all 56583 rows: dhidden rows bitwise those of the 14 chunked
+    calls (row-local arithmetic), dweight equal to rounding (one sum over the tokens instead of
+    14 chunk sums added in order), padded dweight rows zero."""
+    assert config4["whole_dH_same"], "whole-pack dhidden differs from the chunked dhidden"
+    record("config4 dweight whole-pack vs chunked (normwise)", config4["whole_dW_rel"])
+    assert config4["whole_dW_rel"] <= 1e-5
+    assert config4["whole_dW_pad"]
 
 
 @pytest.mark.timeout(900)
