@@ -865,86 +865,42 @@ __global__ __launch_bounds__(256) void k_dh_reduce(DhReduceArgs a) {
   *reinterpret_cast<u32x4*>(a.dH + t * a.ldd + n) = u32x4{pk[0], pk[1], pk[2], pk[3]};
 }
 
-// dweight += the tile, straight from registers. The tile is computed transposed (M = hidden
-// columns n, N = vocabulary rows m), so the 4 accumulators r = 4q .. 4q+3 of block (mi, ni) are
-// 4 consecutive hidden columns of one dweight row: lane l holds row
-// m0 + wn*128 + ni*32 + (l & 31), columns n0 + wm*128 + mi*32 + 8q + 4(l >> 5) + 0..3, one
-// 16-byte chunk, which it loads, adds to (old + sum, in fp32) and stores back. Chunks of rows
-// at or past n_real or columns at or past H are masked: they are neither read into a result
-// nor written. The compiler places every wait (loads and stores share one counter).
-constexpr uint32_t DW_MASKED = 0xFFFFFFFFu;
-struct DwTile {
-  uint32_t off[4][4][4];  // [mi][ni][q] byte offset from the tile's first element, or masked
+// dweight += the tile. The tile's rows are vocabulary rows (M: A = G read K-major) and its
+// columns hidden columns (N: B = hgT, K contiguous), so lane l of block (mi, ni) holds hidden
+// column n = wn*128 + ni*32 + (l & 31) of rows m = wm*128 + mi*32 + mfma_row(r, l): one store
+// instruction (fixed mi, ni, r) writes 2 rows x 32 consecutive fp32 columns, two whole
+// 128-byte lines. Stores and the old values' loads go through a buffer resource over the
+// tile's real rows: rows at or past n_real are out of its range, and lanes whose column is at
+// or past H get an offset past the range, so the hardware drops those stores (and reads 0).
+struct DwOut {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t vb[4];    // per block column ni: this lane's byte offset of (row wm*128 + 4(l >> 5),
+                     // column wn*128 + ni*32 + (l & 31)), or DW_OUT_OF_RANGE past column H
+  uint32_t rstride;  // bytes per dweight row
 };
+constexpr uint32_t DW_OUT_OF_RANGE = 0x80000000u;
 
-__device__ __forceinline__ void dw_tile_setup(const DwArgs& a, int m0, int n0, DwTile& t) {
+__device__ __forceinline__ DwOut dw_out(const DwArgs& a, int m0, int n0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
   const int nv = a.n_real - m0 < BM ? (int)(a.n_real - m0) : BM;
   const int nc = a.H - n0 < BN ? a.H - n0 : BN;
+  DwOut o;
+  o.rstride = (uint32_t)(a.lddw * 4);
+  o.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.dW + (int64_t)m0 * a.lddw + n0), (short)0,
+                                             (int)((uint32_t)nv * o.rstride), 0x00020000);
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = wn * 128 + ni * 32 + (lane & 31);
-        const int n = wm * 128 + mi * 32 + 8 * q + 4 * (lane >> 5);
-        t.off[mi][ni][q] = (m < nv && n < nc) ? (uint32_t)(((int64_t)m * a.lddw + n) * 4)
-                                              : DW_MASKED;
-      }
+  for (int ni = 0; ni < 4; ++ni) {
+    const int col = wn * 128 + ni * 32 + (lane & 31);
+    o.vb[ni] = col < nc ? (uint32_t)(wm * 128 + 4 * (lane >> 5)) * o.rstride + (uint32_t)col * 4u
+                        : DW_OUT_OF_RANGE;
+  }
+  return o;
 }
 
-// Old values of block row mi (16 chunks per lane): plain 16-byte loads, a masked chunk reading
-// the tile's first one instead (its value is never stored).
-__device__ __forceinline__ void dw_load(const DwTile& t, const float* base, int mi,
-                                        u32x4 (&v)[16]) {
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t o = t.off[mi][ni][q];
-      v[4 * ni + q] = *reinterpret_cast<const u32x4*>(
-          reinterpret_cast<const unsigned char*>(base) + (o == DW_MASKED ? 0u : o));
-    }
-}
-
-__device__ __forceinline__ void dw_add_store(const f32x16 (&acc)[4][4], const DwTile& t,
-                                             float* base, int mi, const u32x4 (&v)[16]) {
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      u32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // Through a scalar: a bit cast applied to a vector element in place is miscompiled
-        // (the load is narrowed to its first element).
-        const uint32_t old = v[4 * ni + q][e];
-        o[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, old) +
-                                                acc_read(acc[mi][ni][4 * q + e]));
-      }
-      const uint32_t off = t.off[mi][ni][q];
-      if (off != DW_MASKED)
-        *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(base) + off) = o;
-    }
-}
-
-// Every chunk of the tile written with its sum (overwrite mode): no old values are read.
-__device__ __forceinline__ void dw_store(const f32x16 (&acc)[4][4], const DwTile& t, float* base) {
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          o[e] = __builtin_bit_cast(uint32_t, acc_read(acc[mi][ni][4 * q + e]));
-        const uint32_t off = t.off[mi][ni][q];
-        if (off != DW_MASKED)
-          *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(base) + off) = o;
-      }
+// Byte offset of accumulator (mi, ni, r) of this lane (past the range when masked: the row
+// term is below 2^31 and DW_OUT_OF_RANGE is 2^31, so the sum does not wrap).
+__device__ __forceinline__ uint32_t dw_off(const DwOut& o, int mi, int ni, int r) {
+  return o.vb[ni] + (uint32_t)(mi * 32 + 8 * (r >> 2) + (r & 3)) * o.rstride;
 }
 
 // dweight[v, n] += sum_j G[j, v] hgT[n, j] over the scored rows j in ascending order
@@ -961,42 +917,54 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
   int mt, nt;
   vocab_token_tile<4>(tile, a.ntm, a.ntn, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
-  DwTile t;
-  dw_tile_setup(a, m0, n0, t);
-  float* dwt = a.dW + (int64_t)m0 * a.lddw + n0;
   f32x16 acc[4][4];
   zero_acc(acc);
   if (Ts > 0) {
-    // A (tile rows): hgT rows n0 .. (< H), K = scored rows rounded up to whole steps.
-    // B (tile columns): G itself, K-major: rows = scored rows (zero from the count to the next
+    // A (tile rows): G itself, K-major: rows = scored rows (zero from the count to the next
     // whole step), columns m0 .. m0+255 (inside the padded vocabulary capacity).
+    // B (tile columns): hgT rows n0 .. (< H), K = scored rows rounded up to whole steps.
     const int nn = a.H - n0 < BN ? a.H - n0 : BN;
     const int nk = (Ts + dma::BKD - 1) / dma::BKD;
     const int64_t kb = (int64_t)nk * dma::BKD;
-    dma::Loader la;
-    la.init(a.hgT + (int64_t)n0 * a.ldk, (uint64_t)((nn - 1) * a.ldk + kb) * 2);
+    dma::LoaderK la;
+    la.init(a.G + m0, a.ldg, (int)kb - 1, BM);
+    dma::Loader lb;
+    lb.init(a.hgT + (int64_t)n0 * a.ldk, (uint64_t)((nn - 1) * a.ldk + kb) * 2);
 #pragma unroll
     for (int u = 0; u < dma::NI; ++u) {
       const int r = dma::Loader::row_of(u);
-      la.set(u, r < nn ? r : nn - 1, a.ldk);
+      lb.set(u, r < nn ? r : nn - 1, a.ldk);
     }
-    dma::LoaderK lb;
-    lb.init(a.G + m0, a.ldg, (int)kb - 1, BM);
     dma::mainloop(la, lb, 0, nk, smem, acc);
   }
-  if constexpr (OVERWRITE) {
-    dw_store(acc, t, dwt);
-  } else {
-    // Two block rows of old values in flight at a time.
-    u32x4 v0[16], v1[16];
-    dw_load(t, dwt, 0, v0);
-    dw_load(t, dwt, 1, v1);
-    dw_add_store(acc, t, dwt, 0, v0);
-    dw_load(t, dwt, 2, v0);
-    dw_add_store(acc, t, dwt, 1, v1);
-    dw_load(t, dwt, 3, v1);
-    dw_add_store(acc, t, dwt, 2, v0);
-    dw_add_store(acc, t, dwt, 3, v1);
+  const DwOut o = dw_out(a, m0, n0);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    if constexpr (OVERWRITE) {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __builtin_bit_cast(uint32_t, acc_read(acc[mi][ni][r])), o.rsrc,
+              (int)dw_off(o, mi, ni, r), 0, 0);
+    } else {
+      // The block row's 64 old values, then their sums.
+      uint32_t old[4][16];
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          old[ni][r] = __builtin_amdgcn_raw_buffer_load_b32(o.rsrc, (int)dw_off(o, mi, ni, r), 0, 0);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, old[ni][r]) +
+                                               acc_read(acc[mi][ni][r])),
+              o.rsrc, (int)dw_off(o, mi, ni, r), 0, 0);
+    }
   }
 }
 
