@@ -123,7 +123,7 @@ llp_status check_request(const llp_request* req) {
 
 // Workspace regions (byte offsets, each 256-byte aligned).
 struct Ws {
-  size_t count, qctr, scored, pos, tloc, tz, pm, ps, pq, G, hgT, P, total;
+  size_t count, qctr, scored, pos, tloc, tz, pm, ps, pq, G, hgT, P, dbp, total;
   int64_t T_cap, nvt, ldg;
 };
 
@@ -152,6 +152,7 @@ Ws ws_layout(int64_t T, int64_t n_real, int64_t H, int op) {
     w.G = take((size_t)w.T_cap * (size_t)w.ldg * 2);    // G[j][v]
     w.hgT = take((size_t)H * (size_t)w.T_cap * 2);      // scored hidden rows, transposed
     w.P = take((size_t)DH_SPLITS * (size_t)w.T_cap * (size_t)H * 4);
+    w.dbp = take((size_t)(w.T_cap / TILE) * (size_t)w.ldg * 4);   // bias-gradient partials
   }
   w.total = off;
   return w;
@@ -636,6 +637,7 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
     ga.G = G;
     ga.ldg = w.ldg;
     ga.qctr = qctr;
+    ga.dbp = out->dbias != nullptr ? at<float>(workspace, w.dbp) : nullptr;
       LLP_HIP(launch_grad(ga, s), "gradient kernel launch");
 
     DhArgs da{};
@@ -673,8 +675,8 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
 
     if (out->dbias != nullptr) {
       DbArgs ba{};
-      ba.G = G;
-      ba.ldg = w.ldg;
+      ba.dbp = ga.dbp;
+      ba.ldp = w.ldg;
       ba.n_real = n_real;
       ba.count = la.count;
       ba.db = out->dbias;

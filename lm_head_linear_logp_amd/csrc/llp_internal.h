@@ -172,6 +172,8 @@ struct GradArgs {
   uint16_t* G;
   int64_t ldg;
   int32_t* qctr;    // tile-queue counters (QCTR_INTS), zero at launch
+  float* dbp;       // bias-gradient partials [token block][ldg] (column sums of each G tile),
+                    // or null when the request has no bias
 };
 
 struct DhArgs {
@@ -233,8 +235,8 @@ struct TransposeArgs {
 };
 
 struct DbArgs {
-  const uint16_t* G;
-  int64_t ldg;
+  const float* dbp;  // [token block][ldp] partials of the gradient tiles
+  int64_t ldp;
   int64_t n_real;
   const int32_t* count;
   float* db;

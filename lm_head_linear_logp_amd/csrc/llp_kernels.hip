@@ -786,6 +786,15 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
     if (tail) grad_epilogue<true, false, NFB>(acc, a, v0, j0, Ts, smem);
     else grad_epilogue<false, false, NFB>(acc, a, v0, j0, Ts, smem);
   }
+  // Bias gradient: this tile's column sums of the bf16 G it wrote (still staged in LDS as
+  // Gs[token][vocab]), rows in order; rows past the count are zero.
+  if (a.dbp != nullptr) {
+    for (int c = threadIdx.x; c < BM; c += 64 * NW) {
+      float sum = 0.f;
+      for (int tn = 0; tn < BN; ++tn) sum += bf16_to_f32(smem[tn * GT_STRIDE + c]);
+      a.dbp[(int64_t)tb * a.ldg + v0 + c] = sum;
+    }
+  }
 }
 
 // dhidden partials: P[split][j][n] = sum over the split's K range of G[j, k] W[k, n]
@@ -1012,13 +1021,15 @@ __global__ __launch_bounds__(256) void k_transpose(TransposeArgs a) {
   }
 }
 
-// dbias[v] += sum_j G[j, v] over scored rows in order (overwrite: dbias[v] = the sum).
+// dbias[v] (+)= sum over the token blocks tb = 0, 1, ... (in order) of the gradient tiles'
+// column sums dbp[tb][v] (each the sum of the tile's 256 bf16 G values of column v, rows in
+// order). Only the token blocks holding scored rows ran; G is zero past the count.
 __global__ __launch_bounds__(256) void k_dbias(DbArgs a) {
   const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (v >= a.n_real) return;
-  const int Ts = *a.count;
+  const int nb = (*a.count + BN - 1) / BN;
   float s = 0.f;
-  for (int j = 0; j < Ts; ++j) s += bf16_to_f32(a.G[(int64_t)j * a.ldg + v]);
+  for (int tb = 0; tb < nb; ++tb) s += a.dbp[(int64_t)tb * a.ldp + v];
   a.db[v] = a.overwrite ? s : a.db[v] + s;
 }
 

@@ -126,6 +126,7 @@ hipError_t launch_grad(const GradArgs& a, hipStream_t) {
   // G rows up to the next whole K step past the count, every vocabulary tile's columns.
   rows(a.G, Tc, a.ldg, (int64_t)a.nvt * 256);
   extent(a.qctr, QCTR_INTS);
+  if (a.dbp) rows(a.dbp, a.ntb, a.ldg, (int64_t)a.nvt * 256);
   return a.ldg >= (int64_t)a.nvt * 256 ? hipSuccess : hipErrorInvalidValue;
 }
 hipError_t launch_dh(const DhArgs& a, hipStream_t) {
@@ -160,6 +161,7 @@ hipError_t launch_transpose(const TransposeArgs& a, int64_t nrows, hipStream_t) 
 hipError_t launch_dbias(const DbArgs& a, hipStream_t) {
   ++g_launches;
   extent(a.db, a.n_real);
+  if (a.n_real > 0) extent(a.dbp, a.n_real);   // at least the first token block's row
   return hipSuccess;
 }
 hipError_t launch_zero_rows(const ZeroArgs& a, hipStream_t) {
