@@ -256,28 +256,41 @@ def gpu_clock_sampler(device_index: int = 0):
     return th.start, stop
 
 
-def measure_vendor_gemm(h, W, stream, reps=10):
+def measure_vendor_gemm(h, W, stream, fwd, reps=20):
     """Context for the forward's roofline fraction: the vendor library's plain GEMM of the same
     operands (torch.matmul -> hipBLASLt), h [4096, 4096] x W^T over the padded vocabulary, bf16
     logits out and no epilogue. It is not part of the path; it shows the MFMA rate a tuned
-    library reaches on this shape under the chip's power limit. HIP events on the stream."""
+    library reaches on this shape under the chip's power limit. The clock takes tens of
+    milliseconds to settle after a change of load, so both kernels first run 15 times, then
+    `reps` pairs (vendor GEMM, fused forward) alternate, each call timed with HIP events on the
+    stream; medians are reported, so the two figures are taken under the same conditions."""
     import torch
     out = torch.empty((h.shape[0], W.shape[0]), dtype=torch.bfloat16, device=h.device)
     wt = W.t()
-    torch.matmul(h, wt, out=out)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(reps):
-        torch.matmul(h, wt, out=out)
-    b.record(stream)
+    gemm = lambda: torch.matmul(h, wt, out=out)
+    for _ in range(15):
+        gemm()
+        fwd()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        gemm()
+        ev[2 * i + 1].record(stream)
+        fwd()
+        ev[2 * i + 2].record(stream)
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
+    d = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(2 * reps)])
+    g_ms, f_ms = float(np.median(d[0::2])), float(np.median(d[1::2]))
     del out
     flop = 2.0 * h.shape[0] * h.shape[1] * W.shape[0]
-    tf = flop / (ms * 1e-3) / 1e12
+    tf = flop / (g_ms * 1e-3) / 1e12
     return {"vendor_gemm": {"what": "torch.matmul (hipBLASLt) of h [4096, 4096] by W^T "
-                                    "[4096, 151936], bf16 out, no epilogue",
-                            "us": ms * 1e3, "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS}}
+                                    "[4096, 151936], bf16 out, no epilogue; median of 20 calls "
+                                    "alternating with the fused forward after 15 warm-up pairs",
+                            "us": g_ms * 1e3, "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS,
+                            "fused_forward_alternating_us": f_ms * 1e3,
+                            "fused_forward_alternating_frac":
+                                2.0 * T * H * VR / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
 
 
 def measure_next_rows(llp, logits, rids, rtg, shards, stream, busy, reps=10):
@@ -556,10 +569,30 @@ def main():
     ea[1].record(stream)
     torch.cuda.synchronize()
     bwd_acc_ms = float(ea[0].elapsed_time(ea[1])) / 5
-    del mg
+    # The backward of a biased head (fp32 bias ~ N(0, 0.02^2) over the padded vocabulary):
+    # adds the bias gradient, each gradient tile's column sums then their sum over the token
+    # blocks. 1 + 5 calls, dweight and dbias overwritten.
+    bias = torch.from_numpy(
+        (synth.rng(2, 71).standard_normal(VP) * 0.02).astype(np.float32)).cuda()
+    dbias = torch.empty(VP, dtype=torch.float32, device="cuda")
+    mgb = llp.merge([llp.forward(h, W, tg, temperature=TAU, real_vocab=VR, padded_vocab=VP,
+                                 bias=bias)])
+
+    def bwd_bias():
+        llp.backward(h, W, tg, mgb["lse"], dlogp, temperature=TAU, real_vocab=VR,
+                     padded_vocab=VP, bias=bias, dweight=dW, dhidden=dH, dbias=dbias,
+                     overwrite=True)
+    bwd_bias()
+    ea[0].record(stream)
+    for _ in range(5):
+        bwd_bias()
+    ea[1].record(stream)
+    torch.cuda.synchronize()
+    bwd_bias_ms = float(ea[0].elapsed_time(ea[1])) / 5
+    del mg, mgb, bias, dbias
     log(f"phases (ms): forward {fwd_ms:.3f} merge {merge_ms:.3f} backward {bwd_ms:.3f} "
         f"top-p {topp_ms:.3f}; step {ms_per_step:.3f} (host wall {1e3 * wall / args.steps:.3f}); "
-        f"backward with dweight accumulated {bwd_acc_ms:.3f}")
+        f"backward with dweight accumulated {bwd_acc_ms:.3f}, with a bias {bwd_bias_ms:.3f}")
 
     flop_fwd = 2.0 * T * H * VR
     ach_fwd = flop_fwd / (fwd_ms * 1e-3) / 1e12
@@ -602,6 +635,10 @@ def main():
         "backward_accumulate": {"ms": bwd_acc_ms, "tflops": flop_bwd / (bwd_acc_ms * 1e-3) / 1e12,
                                 "what": "llp_backward with dweight += G^T h (later chunks of a "
                                         "step), 5 calls after the timed steps"},
+        "backward_with_bias": {"ms": bwd_bias_ms,
+                               "what": "llp_backward of the same rows with an fp32 bias "
+                                       "[151936] and its gradient, dweight and dbias "
+                                       "overwritten, 5 calls after the timed steps"},
         "forward_backward_tflops": (flop_fwd + flop_bwd) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12,
         "top_p": {"us": topp_ms * 1e3, "algorithmic_bytes": topp_bytes,
                   "GBps": topp_bytes / (topp_ms * 1e-3) / 1e9, "peak_GBps": PEAK_HBM_GBS},
@@ -613,7 +650,9 @@ def main():
         res.update(measure_config4(
             llp, W, stream,
             busy=lambda: llp.forward(h, W, tg, temperature=TAU, real_vocab=VR, padded_vocab=VP)))
-    res.update(measure_vendor_gemm(h, W, stream))
+    res.update(measure_vendor_gemm(
+        h, W, stream,
+        lambda: llp.forward(h, W, tg, temperature=TAU, real_vocab=VR, padded_vocab=VP)))
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_rows} rows")
         del W, h, logits, dW, dH
