@@ -682,6 +682,9 @@ constexpr int BWDG_LDS_BYTES = GRAD_LDS_BYTES > dma::LDS_BYTES ? GRAD_LDS_BYTES 
 
 // Writes the staged bf16 tile Gs[token][vocab] (LDS) as G rows, including the zero rows from
 // the count up to the next whole K step (the dweight product reads G K-major in steps of 64).
+// Non-temporal stores: G (1.24 GB at T = 4096) is far larger than the caches, so its lines
+// would be gone before the next kernels read them; cached, they would evict operand lines
+// that other tiles re-read (the stores as NT measured ~0.6% off the backward).
 template <int NTHR>
 __device__ __forceinline__ void grad_store(const GradArgs& a, int v0, int j0, int Ts,
                                            const uint16_t* smem) {
@@ -691,8 +694,8 @@ __device__ __forceinline__ void grad_store(const GradArgs& a, int v0, int j0, in
     const int tn = idx >> 5, c = idx & 31;
     const int j = j0 + tn;
     if (j < tpad)
-      *reinterpret_cast<u32x4*>(a.G + (int64_t)j * a.ldg + v0 + c * 8) =
-          *reinterpret_cast<const u32x4*>(smem + tn * GT_STRIDE + c * 8);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(smem + tn * GT_STRIDE + c * 8),
+                                  reinterpret_cast<u32x4*>(a.G + (int64_t)j * a.ldg + v0 + c * 8));
   }
 }
 
@@ -881,6 +884,7 @@ __global__ __launch_bounds__(256) void k_dh_reduce(DhReduceArgs a) {
 // 128-byte lines. Stores and the old values' loads go through a buffer resource over the
 // tile's real rows: rows at or past n_real are out of its range, and lanes whose column is at
 // or past H get an offset past the range, so the hardware drops those stores (and reads 0).
+// The dweight traffic is non-temporal (cache policy NT): it is touched once per call.
 struct DwOut {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t vb[4];    // per block column ni: this lane's byte offset of (row wm*128 + 4(l >> 5),
@@ -888,6 +892,7 @@ struct DwOut {
   uint32_t rstride;  // bytes per dweight row
 };
 constexpr uint32_t DW_OUT_OF_RANGE = 0x80000000u;
+constexpr int DW_CPOL = 2;  // buffer instruction cache policy: NT
 
 __device__ __forceinline__ DwOut dw_out(const DwArgs& a, int m0, int n0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
@@ -956,7 +961,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
         for (int r = 0; r < 16; ++r)
           __builtin_amdgcn_raw_buffer_store_b32(
               __builtin_bit_cast(uint32_t, acc_read(acc[mi][ni][r])), o.rsrc,
-              (int)dw_off(o, mi, ni, r), 0, 0);
+              (int)dw_off(o, mi, ni, r), 0, DW_CPOL);
     } else {
       // The block row's 64 old values, then their sums.
       uint32_t old[4][16];
@@ -964,7 +969,8 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
       for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          old[ni][r] = __builtin_amdgcn_raw_buffer_load_b32(o.rsrc, (int)dw_off(o, mi, ni, r), 0, 0);
+          old[ni][r] = __builtin_amdgcn_raw_buffer_load_b32(o.rsrc, (int)dw_off(o, mi, ni, r), 0,
+                                                            DW_CPOL);
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -972,7 +978,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 
           __builtin_amdgcn_raw_buffer_store_b32(
               __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, old[ni][r]) +
                                                acc_read(acc[mi][ni][r])),
-              o.rsrc, (int)dw_off(o, mi, ni, r), 0, 0);
+              o.rsrc, (int)dw_off(o, mi, ni, r), 0, DW_CPOL);
     }
   }
 }
