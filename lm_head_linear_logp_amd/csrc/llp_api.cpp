@@ -138,7 +138,7 @@ Ws ws_layout(int64_t T, int64_t n_real, int64_t H, int op) {
     off += (size_t)round_up((int64_t)(bytes > 0 ? bytes : 1), 256);
     return o;
   };
-  w.count = take(256);
+  w.count = take((size_t)(1 + layout_blocks(T)) * 4);   // 256 bytes up to 63 layout blocks
   w.qctr = take(256);   // tile-queue counters: QCTR_INTS per GEMM kernel of the call
   w.scored = take((size_t)w.T_cap * 4);
   w.pos = take((size_t)w.T_cap * 4);

@@ -19,6 +19,12 @@ constexpr size_t SCRATCH_BYTES = size_t(32) << 20;
 constexpr int MAX_DEVICES = 64;
 constexpr int KSTEP = 64;  // K depth of one pipelined GEMM step
 constexpr int QCTR_INTS = 16;  // tile-queue counters per GEMM kernel launch (llp_tile.hpp)
+// Rows per workgroup of the layout scan when it takes several; up to that many rows one
+// workgroup scans them all.
+constexpr int64_t LAYOUT_BLOCK_ROWS = 16384;
+inline int64_t layout_blocks(int64_t T) {
+  return T > LAYOUT_BLOCK_ROWS ? (T + LAYOUT_BLOCK_ROWS - 1) / LAYOUT_BLOCK_ROWS : 1;
+}
 
 struct LayoutArgs {
   int64_t T;
@@ -28,7 +34,7 @@ struct LayoutArgs {
   int32_t world;
   const int64_t* targets;
   int64_t offset, n_real, real_vocab;
-  int32_t* count;   // [1] number of scored rows
+  int32_t* count;   // [1 + layout_blocks(T)]: scored rows, then per layout block (if several)
   int32_t* scored;  // [T] compact index -> row
   int32_t* pos;     // [T] row -> compact index or -1
   int32_t* tloc;    // [T] compact index -> local target column or -1

@@ -14,35 +14,69 @@
 namespace llp {
 
 // ------------------------------------------------------------------------------------
-// Layout and mask indexing. One workgroup scans the loss mask in order (16 rows per thread and
+// Layout and mask indexing. A workgroup scans the loss mask in order (16 rows per thread and
 // pass) and writes the compact list of scored rows, each row's compact index (-1 when
 // unscored), the target's local column (-1 when outside this shard's real columns), zero
-// outputs for unscored rows, and status bits ([CUDA provider, "Summary"]: the framework keeps token layout and
-// masking; the operator scores unmasked rows only).
+// outputs for unscored rows, and status bits ([CUDA provider, "Summary"]: the framework keeps
+// token layout and masking; the operator scores unmasked rows only). Up to LAYOUT_BLOCK rows
+// one workgroup does it all; beyond, workgroup b takes rows [b, b + 1) * LAYOUT_BLOCK and
+// starts its compact indices after the scored rows of the blocks before it, counted by
+// k_layout_count in a launch of its own (no workgroup waits for another). Either way row t's
+// compact index is the number of scored rows before t.
+// count[0] = the number of scored rows; count[1 + b] = block b's (multi-block launch only).
 // ------------------------------------------------------------------------------------
 constexpr int LAYOUT_THREADS = 1024, LAYOUT_ROWS = 16;   // rows per thread per pass
+constexpr int64_t LAYOUT_BLOCK = (int64_t)LAYOUT_THREADS * LAYOUT_ROWS;
+static_assert(LAYOUT_BLOCK == LAYOUT_BLOCK_ROWS, "layout block shared with the host");
+
+__device__ __forceinline__ bool layout_scored(const LayoutArgs& a, int64_t t) {
+  return t < a.T && (a.mask == nullptr || a.mask[t] != 0);
+}
+
+__global__ __launch_bounds__(LAYOUT_THREADS) void k_layout_count(LayoutArgs a) {
+  __shared__ int wsum[LAYOUT_THREADS / 64];
+  const int64_t t0 = (int64_t)blockIdx.x * LAYOUT_BLOCK + (int64_t)threadIdx.x * LAYOUT_ROWS;
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < LAYOUT_ROWS; ++k) cnt += layout_scored(a, t0 + k) ? 1 : 0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tot = 0;
+    for (int w = 0; w < LAYOUT_THREADS / 64; ++w) tot += wsum[w];
+    a.count[1 + blockIdx.x] = tot;
+  }
+}
 
 __global__ __launch_bounds__(LAYOUT_THREADS) void k_layout(LayoutArgs a) {
   __shared__ int wsum[LAYOUT_THREADS / 64];
   __shared__ int carry_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int blk = blockIdx.x;
   int status = 0;
-  if (tid == 0) carry_s = 0;
+  if (tid == 0) {
+    int c = 0;
+    for (int b = 0; b < blk; ++b) c += a.count[1 + b];   // scored rows of the blocks before
+    carry_s = c;
+  }
   // The tile-queue counters of the GEMM kernels that follow on this stream start at 0.
-  if (tid < a.nqctr) a.qctr[tid] = 0;
+  if (blk == 0 && tid < a.nqctr) a.qctr[tid] = 0;
   __syncthreads();
+  // One workgroup: every pass; several: this block's one pass.
+  const int64_t first = (int64_t)blk * LAYOUT_BLOCK;
+  const int64_t end = gridDim.x == 1 ? a.T : first + LAYOUT_BLOCK;
   // Each pass covers LAYOUT_THREADS * LAYOUT_ROWS rows; thread tid takes LAYOUT_ROWS
   // consecutive ones. Its scored rows get consecutive compact indices after those of all
   // lower threads (an exclusive scan of the per-thread counts), so the compaction keeps row
   // order, as a serial scan would.
-  for (int64_t base = 0; base < a.T; base += (int64_t)LAYOUT_THREADS * LAYOUT_ROWS) {
+  for (int64_t base = first; base < end && base < a.T; base += LAYOUT_BLOCK) {
     const int64_t t0 = base + (int64_t)tid * LAYOUT_ROWS;
     uint32_t bits = 0;
 #pragma unroll
-    for (int k = 0; k < LAYOUT_ROWS; ++k) {
-      const int64_t t = t0 + k;
-      if (t < a.T && (a.mask == nullptr || a.mask[t] != 0)) bits |= 1u << k;
-    }
+    for (int k = 0; k < LAYOUT_ROWS; ++k)
+      if (layout_scored(a, t0 + k)) bits |= 1u << k;
     const int cnt = __popc(bits);
     int incl = cnt;  // inclusive scan over the wave
 #pragma unroll
@@ -87,8 +121,8 @@ __global__ __launch_bounds__(LAYOUT_THREADS) void k_layout(LayoutArgs a) {
     }
     __syncthreads();
   }
-  if (tid == 0) a.count[0] = carry_s;
-  if (a.cu_seqlens != nullptr) {
+  if (blk == gridDim.x - 1 && tid == 0) a.count[0] = carry_s;
+  if (blk == 0 && a.cu_seqlens != nullptr) {
     for (int i = tid; i <= a.num_seqs; i += LAYOUT_THREADS) {
       const int c = a.cu_seqlens[i];
       if (i == 0 && c != 0) status |= LLP_STATUS_LAYOUT_INVALID;
@@ -1292,7 +1326,13 @@ __global__ __launch_bounds__(256) void k_keep(KeepArgs a) {
 }
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_layout, dim3(1), dim3(LAYOUT_THREADS), 0, s, a);
+  const int64_t nb = layout_blocks(a.T);
+  if (nb > 1) {
+    hipLaunchKernelGGL(k_layout_count, dim3((unsigned)nb), dim3(LAYOUT_THREADS), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_layout, dim3((unsigned)nb), dim3(LAYOUT_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -74,7 +74,7 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t) {
   extent(a.mask, a.T);
   extent(a.targets, a.T);
   if (a.cu_seqlens) extent(a.cu_seqlens, (int64_t)a.num_seqs + 1);
-  extent(a.count, 1);
+  extent(a.count, 1 + (layout_blocks(a.T) > 1 ? layout_blocks(a.T) : 0));
   extent(a.scored, a.T);
   extent(a.pos, a.T);
   extent(a.tloc, a.T);

@@ -523,3 +523,45 @@ def test_forward_batch_size_invariance_bitwise(llp):
     check_forward({k: a[k][torch.from_numpy(pick).cuda()] for k in ("logp", "entropy", "lse",
                                                                     "in_range")},
                   ref, case["mask"][pick], "batch size")
+
+
+@pytest.mark.parametrize("T", [16385, 3 * 16384 + 1234])
+def test_layout_scan_over_several_blocks_bitwise(llp, T):
+    """Beyond 16384 rows the layout scan takes one workgroup per 16384-row block, each block's
+    compact indices following the scored rows counted in the blocks before it. With masked
+    and scored runs that cross the block edges, the forward outputs and the dhidden rows are
+    bitwise those of the same rows in calls of at most 16384 rows (one workgroup), the status
+    word stays clear, and rows at the block edges match the oracle."""
+    H, Vr, Vp, tau = 64, 700, 768, 0.7
+    case = synth.small_case(T, H, Vr, Vp, tau, case_id=90 + T % 7, mask_frac=0.3, w_std=0.05)
+    mask = case["mask"].copy()
+    mask[16000:16384 + 300] = 0                  # masked across the first block edge
+    mask[min(T, 32000):min(T, 33500)] = 1        # scored across the second
+    case = dict(case, mask=mask)
+    say(f"layout scan: T={T} ({-(-T // 16384)} blocks), {int(mask.sum())} scored rows")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a = run_forward(llp, case, status=st)
+    assert int(st.item()) == 0
+    cuts = sorted({c for c in (0, 7000, 16384, 16385, 30000, 40000) if c < T} | {T})
+    dl = synth.rng(90, 1).standard_normal(T).astype(np.float32) * mask
+    dH = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty((Vp, H), dtype=torch.float32, device="cuda")
+    run_backward(llp, case, host(a["lse"]), dl, dhidden=dH, dweight=dW, overwrite=True)
+    dH_all = host(dH.float())
+    for c0, c1 in zip(cuts[:-1], cuts[1:]):
+        sub = dict(case, T=c1 - c0, hidden=case["hidden"][c0:c1], targets=case["targets"][c0:c1],
+                   mask=case["mask"][c0:c1])
+        b = run_forward(llp, sub)
+        for k in ("logp", "entropy", "lse", "target_logit", "in_range"):
+            np.testing.assert_array_equal(host(a[k])[c0:c1].view(np.uint8),
+                                          host(b[k]).view(np.uint8), err_msg=f"{k} rows {c0}:{c1}")
+        dHs = torch.empty((c1 - c0, H), dtype=torch.bfloat16, device="cuda")
+        run_backward(llp, sub, host(b["lse"]), dl[c0:c1], dhidden=dHs, dweight=dW, overwrite=True)
+        np.testing.assert_array_equal(dH_all[c0:c1], host(dHs.float()), err_msg=f"dH {c0}:{c1}")
+    pick = np.unique([r for r in (0, 16383, 16384, 16385, 32767, 32768, 49151, 49152, T - 1)
+                      if r < T])
+    ref = oracle.forward(case["hidden"][pick], case["weight"], None, tau, case["targets"][pick],
+                         mask[pick], Vr)
+    check_forward({k: a[k][torch.from_numpy(pick).cuda()] for k in ("logp", "entropy", "lse",
+                                                                    "in_range")},
+                  ref, mask[pick], f"layout T={T}")
