@@ -565,3 +565,44 @@ def test_layout_scan_over_several_blocks_bitwise(llp, T):
     check_forward({k: a[k][torch.from_numpy(pick).cuda()] for k in ("logp", "entropy", "lse",
                                                                     "in_range")},
                   ref, mask[pick], f"layout T={T}")
+
+
+def test_row_strides_wider_than_H_bitwise(llp):
+    """hidden, weight, dhidden and dweight given as views into wider row-major buffers (row
+    strides H + 72, H + 136, H + 40 and H + 12 elements). The padding columns of the inputs
+    hold 1e4, so reading any of them would change every result; the outputs' padding holds a
+    sentinel that must come back untouched. Forward outputs, dhidden and dweight are bitwise
+    those of contiguous tensors."""
+    T, H, Vr, Vp, tau = 300, 256, 1000, 1024, 0.7
+    case = synth.small_case(T, H, Vr, Vp, tau, case_id=77, mask_frac=0.2, with_bias=True,
+                            w_std=0.05)
+    say("row strides wider than H: forward and backward on views")
+    h, W = dev_bf16(case["hidden"]), dev_bf16(case["weight"])
+    hw = torch.full((T, H + 72), 1e4, dtype=torch.bfloat16, device="cuda")
+    ww = torch.full((Vp, H + 136), 1e4, dtype=torch.bfloat16, device="cuda")
+    hw[:, :H] = h
+    ww[:, :H] = W
+    hv, wv = hw[:, :H], ww[:, :H]
+    assert hv.stride(0) == H + 72 and wv.stride(0) == H + 136
+    kw = dict(temperature=tau, bias=dev_bf16(case["bias"]), loss_mask=dev(case["mask"]),
+              real_vocab=Vr, padded_vocab=Vp)
+    tg = dev(case["targets"])
+    a = llp.forward(h, W, tg, **kw)
+    b = llp.forward(hv, wv, tg, **kw)
+    torch.cuda.synchronize()
+    for k in ("logp", "entropy", "lse", "target_logit", "in_range"):
+        assert bytes_equal(a[k], b[k]), k
+    dl = dev(synth.rng(77, 3).standard_normal(T).astype(np.float32), torch.float32)
+    dH = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty((Vp, H), dtype=torch.float32, device="cuda")
+    llp.backward(h, W, tg, a["lse"], dl, dhidden=dH, dweight=dW, overwrite=True, **kw)
+    dHw = torch.full((T, H + 40), -7.0, dtype=torch.bfloat16, device="cuda")
+    dWw = torch.full((Vp, H + 12), float("nan"), dtype=torch.float32, device="cuda")
+    llp.backward(hv, wv, tg, b["lse"], dl, dhidden=dHw[:, :H], dweight=dWw[:, :H],
+                 overwrite=True, **kw)
+    torch.cuda.synchronize()
+    assert bytes_equal(dH, dHw[:, :H].contiguous()) and bytes_equal(dW, dWw[:, :H].contiguous())
+    assert torch.all(dHw[:, H:] == -7.0) and torch.all(torch.isnan(dWw[:, H:]))
+    ref = oracle.forward(case["hidden"], case["weight"], case["bias"], tau, case["targets"],
+                         case["mask"], Vr)
+    check_forward(b, ref, case["mask"], "strided views")
