@@ -56,10 +56,13 @@ __global__ __launch_bounds__(LAYOUT_THREADS) void k_layout(LayoutArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blk = blockIdx.x;
   int status = 0;
-  if (tid == 0) {
+  if (wave == 0) {
+    // Scored rows of the blocks before this one (integer sums: exact in any order).
     int c = 0;
-    for (int b = 0; b < blk; ++b) c += a.count[1 + b];   // scored rows of the blocks before
-    carry_s = c;
+    for (int b = lane; b < blk; b += 64) c += a.count[1 + b];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+    if (lane == 0) carry_s = c;
   }
   // The tile-queue counters of the GEMM kernels that follow on this stream start at 0.
   if (blk == 0 && tid < a.nqctr) a.qctr[tid] = 0;

@@ -606,3 +606,25 @@ def test_row_strides_wider_than_H_bitwise(llp):
     ref = oracle.forward(case["hidden"], case["weight"], case["bias"], tau, case["targets"],
                          case["mask"], Vr)
     check_forward(b, ref, case["mask"], "strided views")
+
+
+def test_layout_scan_past_64_blocks_bitwise(llp):
+    """Past 64 layout blocks (T > 64 * 16384 rows) each workgroup's count of the scored rows
+    before it is summed by the 64 lanes of a wave in strides. 1,065,037 rows (66 blocks) with
+    a small projection: the forward outputs are bitwise those of separate calls over row
+    ranges around the 64-block edge and at the tail, and the status word stays clear."""
+    T, H, Vr, Vp, tau = 65 * 16384 + 77, 64, 200, 256, 0.7
+    case = synth.small_case(T, H, Vr, Vp, tau, case_id=95, mask_frac=0.4, w_std=0.05)
+    say(f"layout scan past 64 blocks: T={T}, {int(case['mask'].sum())} scored rows")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a = run_forward(llp, case, status=st)
+    assert int(st.item()) == 0
+    for c0, c1 in ((0, 9000), (64 * 16384 - 5000, 64 * 16384 + 5000), (T - 12000, T)):
+        sub = dict(case, T=c1 - c0, hidden=case["hidden"][c0:c1], targets=case["targets"][c0:c1],
+                   mask=case["mask"][c0:c1])
+        b = run_forward(llp, sub)
+        for k in ("logp", "entropy", "lse", "target_logit", "in_range"):
+            np.testing.assert_array_equal(host(a[k])[c0:c1].view(np.uint8),
+                                          host(b[k]).view(np.uint8), err_msg=f"{k} rows {c0}:{c1}")
+    m = case["mask"].astype(bool)
+    assert np.all(host(a["logp"])[~m] == 0) and np.all(host(a["in_range"])[m] == 1)
