@@ -67,6 +67,7 @@ def test_noalloc_matches_forward_on_consecutive_calls():
     llp.open(0)
     cases = [
         # (T, H, real V, padded V, bias, masked fraction, entropy): largest first.
+        (18432, 64, 37717, 37984, None, 0.25, True),       # at the limit, 2 layout blocks
         (4608, 64, 151669, 151936, None, 0.0, True),       # at the scratch limit
         (3000, 512, 20000, 20480, "f32", 0.2, True),
         (700, 256, 3000, 3072, None, 0.3, False),
