@@ -158,12 +158,14 @@ Ws ws_layout(int64_t T, int64_t n_real, int64_t H, int op) {
   return w;
 }
 
-llp_status check_device() {
+// The current device must have been opened; `num_cus` (optional) receives its compute units.
+llp_status check_device(int* num_cus = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(LLP_ERR_HIP, "hipGetDevice failed");
   std::lock_guard<std::mutex> lk(g_mu);
   LLP_CHECK(dev >= 0 && dev < kMaxDevices && g_opened[dev], LLP_ERR_INVALID_ARGUMENT,
             "llp_open has not succeeded on the current device %d", dev);
+  if (num_cus) *num_cus = g_num_cus[dev];
   return LLP_OK;
 }
 
@@ -343,7 +345,7 @@ LLP_API llp_status llp_open(int32_t device, llp_info* info) {
     snprintf(info->version, sizeof(info->version), "%s", LLP_VERSION);
     snprintf(info->arch, sizeof(info->arch), "%.31s", prop.gcnArchName);
     snprintf(info->route, sizeof(info->route),
-             "hip-gfx950 mfma32x32x16bf16 tile256x256 bk64 lds-dma-2stage fwd-w8 bwd-w4 xcd8 vgroup8 dhsplit%d",
+             "hip-gfx950 mfma32x32x16bf16 tile256x256 bk64 lds-dma-2stage fwd-w8-persistent bwd-w4 xcd8 vgroup8 dhsplit%d",
              DH_SPLITS);
     info->max_replay_ids = LLP_MAX_REPLAY_IDS;
     info->num_cus = prop.multiProcessorCount;
@@ -388,7 +390,8 @@ llp_status forward_impl(const llp_request* req, const llp_partials* out, void* w
             "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, w.total);
   LLP_CHECK(workspace != nullptr && aligned(workspace, 256), LLP_ERR_INVALID_ARGUMENT,
             "workspace must be non-NULL and 256-byte aligned");
-  st = check_device();
+  int num_cus = 0;
+  st = check_device(&num_cus);
   if (st != LLP_OK) return st;
   if (T == 0) return LLP_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -436,6 +439,7 @@ llp_status forward_impl(const llp_request* req, const llp_partials* out, void* w
   fa.pq = at<float>(workspace, w.pq);
   fa.tz = at<float>(workspace, w.tz);
   fa.pstride = w.T_cap;
+  fa.workers = num_cus;
   LLP_HIP(launch_fwd(fa, s), "forward kernel launch");
 
   CombineArgs ca{};

@@ -220,12 +220,13 @@ constexpr int BIAS_NONE = 0, BIAS_BF16 = 1, BIAS_F32 = 2;
 // 64 values of its wave's 128 columns (mi, r), the lane pair, then the two column halves.
 template <bool TAIL, int NFB>
 __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][NFB], const FwdArgs& a, int vt,
-                                             int v0, int j0, int Ts, uint16_t* smem) {
+                                             int v0, int j0, int Ts, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   constexpr int TW = 32 * NFB;  // tokens per wave
   const int vbase = v0 + wm * 128;
-  float* red = reinterpret_cast<float*>(smem);  // [6][256]: max0 max1 s0 s1 q0 q1
+  // red: [6][256] in LDS: max0 max1 s0 s1 q0 q1. The exchange between waves goes through LDS
+  // only, so the barriers wait for LDS alone (DMA loads of a next tile may be in flight).
   // Pass 1: per-token max of x over this lane's 64 columns, the lane pair (l, l^32) and the two
   // waves holding the tile's two column halves. z = x * c1 with c1 > 0 and rounding is
   // monotonic, so fl(max x * c1) is the max of z.
@@ -248,7 +249,7 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][NFB], const 
     mx[ni] = fmaxf(mx[ni], __shfl_xor(mx[ni], 32));
     if (lane < 32) red[wm * 256 + wn * TW + ni * 32 + lane] = mx[ni];
   }
-  __syncthreads();
+  dma::lds_barrier();
   // Pass 2: s = sum 2^d2, q = sum 2^d2 * d2 with d2 = (z - M) log2(e) = x c1 log2(e) - M log2(e).
   const float c1l = a.c1 * kLog2e;
   float ml[NFB];
@@ -286,7 +287,7 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][NFB], const 
       red[1024 + wm * 256 + tn] = qv[ni];
     }
   }
-  __syncthreads();
+  dma::lds_barrier();
 #pragma unroll
   for (int ni = 0; ni < NFB; ++ni) {
     const int tn = wn * TW + ni * 32 + (lane & 31);
@@ -326,9 +327,13 @@ __device__ __forceinline__ void weight_hidden_loaders(const uint16_t* W, int64_t
                                                       dma::LoaderT<NW>& la, dma::LoaderT<NW>& lb) {
   const int nv = n_real - v0 < BM ? (int)(n_real - v0) : BM;
   const int nj = Ts - j0 < BN ? Ts - j0 : BN;
-  const int64_t h0 = scored[j0];
+  // One address for the whole wave: readfirstlane keeps the resources in scalar registers also
+  // where the compiler reads `scored` with vector loads (after stores it cannot prove
+  // disjoint), which would otherwise put every DMA instruction in a per-lane loop.
+  const int64_t h0 = __builtin_amdgcn_readfirstlane(scored[j0]);
+  const int64_t hl = __builtin_amdgcn_readfirstlane(scored[j0 + nj - 1]);
   la.init(W + (int64_t)v0 * ldw, (uint64_t)((nv - 1) * ldw + H) * 2);
-  lb.init(h + h0 * ldh, (uint64_t)((scored[j0 + nj - 1] - h0) * ldh + H) * 2);
+  lb.init(h + h0 * ldh, (uint64_t)((hl - h0) * ldh + H) * 2);
 #pragma unroll
   for (int u = 0; u < dma::LoaderT<NW>::NIW; ++u) {
     const int r = dma::LoaderT<NW>::row_of(u);
@@ -337,41 +342,108 @@ __device__ __forceinline__ void weight_hidden_loaders(const uint16_t* W, int64_t
   }
 }
 
-// The epilogue reuses the pipeline's LDS for 6 x 256 fp32 partials.
-static_assert(6 * 256 * 4 <= dma::LDS_BYTES, "forward epilogue LDS");
+// The forward's LDS: the pipeline's two stages, then the epilogue's 6 x 256 fp32 partials. One
+// array, not two: with a second LDS object the compiler can no longer tell the stages' DMA
+// writes from the fragment reads and waits for every DMA load before each read.
+constexpr int FWD_LDS_HALFS = dma::LDS_BYTES / 2 + 6 * 256 * 2;
 static_assert(dma::BKD == KSTEP, "K step shared with the host");
 static_assert(QCTR_INTS > NUM_XCD, "queue counters and the all-empty flag");
 
-// One kernel per bias mode, differing only in how the accumulators start: a run-time choice
-// there makes the compiler spill accumulators in the epilogue.
 // The forward tile runs FWD_WAVES = 8 waves, two per SIMD: each wave holds 128 x 64 outputs (128
 // accumulators), so one wave's LDS reads, DMA issue and barrier waits overlap the other's
 // MFMAs. Every output's MFMA chain and every token's reduction order are those of the 4-wave
-// tile (1 wave per SIMD, 128 x 128 per wave).
+// tile (1 wave per SIMD, 128 x 128 per wave). Kernels come one per bias mode, differing only in
+// how the accumulators start: a run-time choice there makes the compiler spill accumulators in
+// the epilogue.
 constexpr int FWD_WAVES = 8;
 
+template <int BMODE, int NFB>
+__device__ __forceinline__ void fwd_init_acc(f32x16 (&acc)[4][NFB], const FwdArgs& a, int v0) {
+  if constexpr (BMODE == BIAS_NONE) zero_acc(acc);
+  else bias_acc<BMODE == BIAS_F32, NFB>(acc, a.bias, v0, a.n_real);
+}
+
+template <int NFB>
+__device__ __forceinline__ void fwd_tile_epilogue(const f32x16 (&acc)[4][NFB], const FwdArgs& a,
+                                                  int vt, int tb, int Ts, float* red) {
+  const int v0 = vt * BM, j0 = tb * BN;
+  if (v0 + BM > a.n_real) fwd_epilogue<true, NFB>(acc, a, vt, v0, j0, Ts, red);
+  else fwd_epilogue<false, NFB>(acc, a, vt, v0, j0, Ts, red);
+}
+
+// The forward GEMM as persistent workers (the host launches one per compute unit, a multiple
+// of NUM_XCD, when the K steps are even). Worker wi of XCD x runs positions wi, wi + nwx, ... of
+// the XCD's contiguous share of the logical tiles: the order in which one workgroup per tile
+// would start them, without a workgroup launch, address setup and first DMA round trip per
+// tile. The last two K steps of a tile load the first two of the worker's next tile, which
+// land during the epilogue. Tiles past the scored rows are skipped. A tile's arithmetic is
+// that of k_fwd_tiles: results are bitwise the same.
 template <int BMODE, int NW>
 __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_fwd(FwdArgs a) {
   constexpr int NFB = 16 / NW;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
-  // One workgroup per tile in the static XCD order: the forward's tiles are not drawn from
-  // the tile queues. Under the chip's power limit the queues' dynamic tail (its atomics and
-  // surplus workgroups) cost the forward ~5% while they saved the backward kernels ~2%.
+  __shared__ __attribute__((aligned(16))) uint16_t smem[FWD_LDS_HALFS];
+  float* const red = reinterpret_cast<float*>(smem + dma::LDS_BYTES / 2);
+  const int Ts = *a.count;
+  const int ntiles = a.nvt * a.ntb;
+  const int x = blockIdx.x % NUM_XCD, wi = blockIdx.x / NUM_XCD, nwx = gridDim.x / NUM_XCD;
+  const int qf = queue_first(ntiles, x), qs = queue_size(ntiles, x);
+  int q = wi, vt = 0, tb = 0;
+  for (; q < qs; q += nwx) {
+    vocab_token_tile(qf + q, a.nvt, a.ntb, vt, tb);
+    if (tb * BN < Ts) break;
+  }
+  if (q >= qs) return;
+  const int n = a.H / dma::BKD;
+  dma::LoaderT<NW> la, lb, la2, lb2;
+  weight_hidden_loaders<NW>(a.W, a.ldw, a.n_real, vt * BM, a.h, a.ldh, a.scored, tb * BN, Ts,
+                            a.H, la, lb);
+  bool primed = false;
+  for (;;) {
+    int q2 = q + nwx, vt2 = 0, tb2 = 0;
+    for (; q2 < qs; q2 += nwx) {
+      vocab_token_tile(qf + q2, a.nvt, a.ntb, vt2, tb2);
+      if (tb2 * BN < Ts) break;
+    }
+    const bool more = q2 < qs;
+    if (more) {
+      weight_hidden_loaders<NW>(a.W, a.ldw, a.n_real, vt2 * BM, a.h, a.ldh, a.scored, tb2 * BN,
+                                Ts, a.H, la2, lb2);
+    } else {
+      la2 = la;
+      lb2 = lb;
+    }
+    f32x16 acc[4][NFB];
+    fwd_init_acc<BMODE, NFB>(acc, a, vt * BM);
+    dma::mainloop_chain(la, lb, la2, lb2, primed, more, n, smem, acc);
+    fwd_tile_epilogue<NFB>(acc, a, vt, tb, Ts, red);
+    if (!more) break;
+    q = q2;
+    vt = vt2;
+    tb = tb2;
+    la = la2;
+    lb = lb2;
+    primed = true;
+  }
+}
+
+// One workgroup per tile in the static XCD order: the forward for an odd number of K steps,
+// where the persistent workers' stage parity does not carry from one tile to the next.
+template <int BMODE, int NW>
+__global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_fwd_tiles(FwdArgs a) {
+  constexpr int NFB = 16 / NW;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[FWD_LDS_HALFS];
+  float* const red = reinterpret_cast<float*>(smem + dma::LDS_BYTES / 2);
   int vt, tb;
   vocab_token_tile(xcd_remap(blockIdx.x, gridDim.x), a.nvt, a.ntb, vt, tb);
   const int Ts = *a.count;
-  const int j0 = tb * BN, v0 = vt * BM;
-  if (j0 >= Ts) return;
+  if (tb * BN >= Ts) return;
   dma::LoaderT<NW> la, lb;
-  weight_hidden_loaders<NW>(a.W, a.ldw, a.n_real, v0, a.h, a.ldh, a.scored, j0, Ts, a.H, la, lb);
+  weight_hidden_loaders<NW>(a.W, a.ldw, a.n_real, vt * BM, a.h, a.ldh, a.scored, tb * BN, Ts,
+                            a.H, la, lb);
   f32x16 acc[4][NFB];
-  if constexpr (BMODE == BIAS_NONE) zero_acc(acc);
-  else bias_acc<BMODE == BIAS_F32, NFB>(acc, a.bias, v0, a.n_real);
+  fwd_init_acc<BMODE, NFB>(acc, a, vt * BM);
   dma::mainloop(la, lb, 0, a.H / dma::BKD, smem, acc);
-  if (v0 + BM > a.n_real)
-    fwd_epilogue<true, NFB>(acc, a, vt, v0, j0, Ts, smem);
-  else
-    fwd_epilogue<false, NFB>(acc, a, vt, v0, j0, Ts, smem);
+  fwd_tile_epilogue<NFB>(acc, a, vt, tb, Ts, red);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1349,11 +1421,23 @@ static inline unsigned workers(int tiles) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
-  if (a.nvt > 0 && a.ntb > 0) {
-    const dim3 grid(a.nvt * a.ntb), block(64 * FWD_WAVES);
+  if (a.nvt <= 0 || a.ntb <= 0) return hipGetLastError();
+  const int64_t ntiles = (int64_t)a.nvt * a.ntb;
+  const int n = a.H / KSTEP;
+  const dim3 block(64 * FWD_WAVES);
+  if (n >= 2 && n % 2 == 0) {
+    // One worker per compute unit, at most one per tile, in whole XCD rows.
+    int64_t workers = a.workers > 0 && a.workers < ntiles ? a.workers : ntiles;
+    workers = (workers + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+    const dim3 grid((unsigned)workers);
     if (a.bias == nullptr) hipLaunchKernelGGL((k_fwd<BIAS_NONE, FWD_WAVES>), grid, block, 0, s, a);
     else if (a.bias_f32) hipLaunchKernelGGL((k_fwd<BIAS_F32, FWD_WAVES>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_fwd<BIAS_BF16, FWD_WAVES>), grid, block, 0, s, a);
+  } else {
+    const dim3 grid((unsigned)ntiles);
+    if (a.bias == nullptr) hipLaunchKernelGGL((k_fwd_tiles<BIAS_NONE, FWD_WAVES>), grid, block, 0, s, a);
+    else if (a.bias_f32) hipLaunchKernelGGL((k_fwd_tiles<BIAS_F32, FWD_WAVES>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_fwd_tiles<BIAS_BF16, FWD_WAVES>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

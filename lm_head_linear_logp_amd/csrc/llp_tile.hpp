@@ -56,8 +56,8 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 // OVERSUBSCRIBE workgroups per tile, so a faster XCD runs more workgroups and so more tiles; a
 // workgroup that finds every queue empty exits. Which workgroup runs a tile changes nothing in
 // that tile's arithmetic: results are bitwise those of any other assignment. (The forward
-// keeps one workgroup per tile in the static order: there the dynamic tail measured ~5%
-// slower, the backward kernels ~2% faster.)
+// runs persistent workers over the same static order instead: there the dynamic tail
+// measured ~5% slower, the backward kernels ~2% faster.)
 constexpr int OVERSUBSCRIBE_NUM = 5, OVERSUBSCRIBE_DEN = 4;   // workgroups per tile: 1.25
 // A launch's counters (QCTR_INTS of them, llp_internal.h): [0, 8) the queues' dynamic parts,
 // [8] set once every queue is empty.
@@ -519,6 +519,72 @@ __device__ __forceinline__ void mainloop(const LA& la, const LB& lb, int ks0, in
   }
   wait_vmem_le<0>();
   __syncthreads();
+}
+
+// One K step of mainloop with its loaders made explicit: the DMA slots for step s+1 (regions
+// 1-3) take (ln, lbn) at K step kn, those for step s+2 (region 4) take (ld, lbd) at kd.
+template <class LA, class LB, int NFB, bool AK, bool BK>
+__device__ __forceinline__ void chain_step(const LA& ln, const LB& lbn, int kn, const LA& ld,
+                                           const LB& lbd, int kd, uint16_t* cur, uint16_t* nx,
+                                           const Frag<AK, BK, NFB>& f, bf16x8 (&a0)[4],
+                                           bf16x8 (&b0)[NFB], bf16x8 (&a1)[4], bf16x8 (&b1)[NFB],
+                                           f32x16 (&acc)[4][NFB]) {
+  constexpr int NIW = LA::NIW;
+  constexpr int NQ = 2 * NIW, Q4 = NIW, Q1 = NIW;
+  region<Q1, Q4>(ln, lbn, a0, b0, cur, f, 1, a1, b1, nx, kn, acc);
+  region<NQ - Q4 - Q1, Q4 + Q1>(ln, lbn, a1, b1, cur, f, 2, a0, b0, nx, kn, acc);
+  region<0, 0>(ln, lbn, a0, b0, cur, f, 3, a1, b1, nx, kn, acc);
+  wait_vmem_le<0>();
+  lds_barrier();
+  region<Q4, 0>(ld, lbd, a1, b1, nx, f, 0, a0, b0, cur, kd, acc);
+}
+
+// mainloop over K steps 0..n-1 of one tile of a persistent worker (n even, n >= 2): the same
+// steps, schedule and arithmetic, with two differences at the tile's edges.
+//  - `primed`: the tile's step 0 and the first half of its step 1 are already in flight
+//    (issued by the previous tile's call), so the call starts by waiting for them.
+//  - The DMA slots past the tile's last step take the next tile's steps 0 and 1 through
+//    (la2, lb2). The call then returns with them in flight, and they land while this tile's
+//    epilogue runs. With no next tile, the caller passes this tile's loaders as (la2, lb2) and
+//    `more` false: the slots reload the last step (as in mainloop) and all DMA is drained
+//    before returning.
+// The epilogue must not use the two stages (the next tile's loads land there).
+template <class LA, class LB, int NFB>
+__device__ __forceinline__ void mainloop_chain(const LA& la, const LB& lb, const LA& la2,
+                                               const LB& lb2, bool primed, bool more, int n,
+                                               uint16_t* smem, f32x16 (&acc)[4][NFB]) {
+  constexpr bool AK = LA::KMAJOR, BK = LB::KMAJOR;
+  static_assert(LA::NIW == LB::NIW, "both operands take the same loads per wave");
+  constexpr int NQ = 2 * LA::NIW, Q4 = LA::NIW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  Frag<AK, BK, NFB> f;
+  f.init(wave & 1, wave >> 1, lane);
+  if (!primed) {
+    issue_range<0, NQ>(la, lb, smem, 0);
+    issue_range<0, Q4>(la, lb, smem + 2 * STAGE, 1);
+    wait_vmem_le<Q4>();
+  } else {
+    // The previous epilogue's stores and this tile's setup loads are counted too.
+    wait_vmem_le<0>();
+  }
+  lds_barrier();
+  bf16x8 a0[4], b0[NFB], a1[4], b1[NFB];
+  load_frag(smem, smem + STAGE, f, 0, a0, b0);
+  uint16_t* const s0 = smem;
+  uint16_t* const s1 = smem + 2 * STAGE;
+  for (int s = 0; s < n - 2; s += 2) {
+    chain_step(la, lb, s + 1, la, lb, s + 2, s0, s1, f, a0, b0, a1, b1, acc);
+    chain_step(la, lb, s + 2, la, lb, s + 3, s1, s0, f, a0, b0, a1, b1, acc);
+  }
+  // Steps n-2 (stage 0) and n-1 (stage 1), straight-line (a branch here costs the compiler
+  // its in-place accumulators).
+  const int k0 = more ? 0 : n - 1, k1 = more ? 1 : n - 1;
+  chain_step(la, lb, n - 1, la2, lb2, k0, s0, s1, f, a0, b0, a1, b1, acc);
+  chain_step(la2, lb2, k0, la2, lb2, k1, s1, s0, f, a0, b0, a1, b1, acc);
+  if (!more) {
+    wait_vmem_le<0>();
+    __syncthreads();
+  }
 }
 
 }  // namespace dma
