@@ -417,6 +417,8 @@ llp_status forward_impl(const llp_request* req, const llp_partials* out, void* w
   la.out_e = ent;
   la.out_p = out->logp;
   la.status = req->status_word;
+  la.qctr = at<int32_t>(workspace, w.qctr);   // the forward kernel's tile-queue counters
+  la.nqctr = QCTR_INTS;
   LLP_HIP(launch_layout(la, s), "layout kernel launch");
 
   FwdArgs fa{};
@@ -439,6 +441,7 @@ llp_status forward_impl(const llp_request* req, const llp_partials* out, void* w
   fa.pq = at<float>(workspace, w.pq);
   fa.tz = at<float>(workspace, w.tz);
   fa.pstride = w.T_cap;
+  fa.qctr = la.qctr;
   fa.workers = num_cus;
   LLP_HIP(launch_fwd(fa, s), "forward kernel launch");
 

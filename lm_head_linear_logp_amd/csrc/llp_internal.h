@@ -67,6 +67,7 @@ struct FwdArgs {
   float* pq;
   float* tz;
   int64_t pstride;  // row capacity of the partial arrays (ntb * 256)
+  int32_t* qctr;    // tile-queue counters (QCTR_INTS), zero at launch
   int32_t workers;  // host side: persistent workers to launch (the device's compute units)
 };
 

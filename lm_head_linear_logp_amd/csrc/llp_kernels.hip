@@ -342,10 +342,10 @@ __device__ __forceinline__ void weight_hidden_loaders(const uint16_t* W, int64_t
   }
 }
 
-// The forward's LDS: the pipeline's two stages, then the epilogue's 6 x 256 fp32 partials. One
-// array, not two: with a second LDS object the compiler can no longer tell the stages' DMA
+// The forward's LDS: the pipeline's two stages, then the epilogue's 6 x 256 fp32 partials and a
+// word for tile claims. One array, not several: with a second LDS object the compiler can no longer tell the stages' DMA
 // writes from the fragment reads and waits for every DMA load before each read.
-constexpr int FWD_LDS_HALFS = dma::LDS_BYTES / 2 + 6 * 256 * 2;
+constexpr int FWD_LDS_HALFS = dma::LDS_BYTES / 2 + 6 * 256 * 2 + 8;   // + the tile-claim slot
 static_assert(dma::BKD == KSTEP, "K step shared with the host");
 static_assert(QCTR_INTS > NUM_XCD, "queue counters and the all-empty flag");
 
@@ -372,39 +372,54 @@ __device__ __forceinline__ void fwd_tile_epilogue(const f32x16 (&acc)[4][NFB], c
 }
 
 // The forward GEMM as persistent workers (the host launches one per compute unit, a multiple
-// of NUM_XCD, when the K steps are even). Worker wi of XCD x runs positions wi, wi + nwx, ... of
-// the XCD's contiguous share of the logical tiles: the order in which one workgroup per tile
-// would start them, without a workgroup launch, address setup and first DMA round trip per
-// tile. The last two K steps of a tile load the first two of the worker's next tile, which
+// of NUM_XCD, when the K steps are even). XCD x owns a contiguous share of the logical tiles
+// (its queue, as for the backward kernels). Worker wi of the XCD runs positions wi, wi + nwx,
+// ... of the queue's static first three quarters, in the order one workgroup per tile would
+// start them, then claims tiles of the dynamic last quarter one at a time (own XCD first, then
+// the others'), so that workers of a faster XCD take over the tail of a slower one. Against
+// one workgroup per tile this saves each tile's launch, address setup and first DMA round
+// trip: the last two K steps of a tile load the first two of the worker's next tile, which
 // land during the epilogue. Tiles past the scored rows are skipped. A tile's arithmetic is
-// that of k_fwd_tiles: results are bitwise the same.
+// that of k_fwd_tiles, whoever runs it: results are bitwise the same.
 template <int BMODE, int NW>
 __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_fwd(FwdArgs a) {
   constexpr int NFB = 16 / NW;
   __shared__ __attribute__((aligned(16))) uint16_t smem[FWD_LDS_HALFS];
   float* const red = reinterpret_cast<float*>(smem + dma::LDS_BYTES / 2);
+  int* const slot = reinterpret_cast<int*>(red + 6 * 256);
   const int Ts = *a.count;
   const int ntiles = a.nvt * a.ntb;
-  const int x = blockIdx.x % NUM_XCD, wi = blockIdx.x / NUM_XCD, nwx = gridDim.x / NUM_XCD;
-  const int qf = queue_first(ntiles, x), qs = queue_size(ntiles, x);
-  int q = wi, vt = 0, tb = 0;
-  for (; q < qs; q += nwx) {
-    vocab_token_tile(qf + q, a.nvt, a.ntb, vt, tb);
-    if (tb * BN < Ts) break;
-  }
-  if (q >= qs) return;
+  const int x = blockIdx.x % NUM_XCD, nwx = gridDim.x / NUM_XCD;
+  const int qf = queue_first(ntiles, x), s0 = queue_static(queue_size(ntiles, x));
+  int pos = blockIdx.x / NUM_XCD;   // the worker's next static position
+  // The worker's next tile with scored rows: false when there is none.
+  auto next_tile = [&](int& vt, int& tb) -> bool {
+    for (;;) {
+      int t;
+      if (pos < s0) {
+        t = qf + pos;
+        pos += nwx;
+      } else {
+        if (threadIdx.x == 0) *slot = claim_dynamic(a.qctr, ntiles, x);
+        dma::lds_barrier();
+        t = *slot;
+        dma::lds_barrier();   // every wave has read the slot before the next claim writes it
+        if (t < 0) return false;
+      }
+      vocab_token_tile(t, a.nvt, a.ntb, vt, tb);
+      if (tb * BN < Ts) return true;
+    }
+  };
+  int vt = 0, tb = 0;
+  if (!next_tile(vt, tb)) return;
   const int n = a.H / dma::BKD;
   dma::LoaderT<NW> la, lb, la2, lb2;
   weight_hidden_loaders<NW>(a.W, a.ldw, a.n_real, vt * BM, a.h, a.ldh, a.scored, tb * BN, Ts,
                             a.H, la, lb);
   bool primed = false;
   for (;;) {
-    int q2 = q + nwx, vt2 = 0, tb2 = 0;
-    for (; q2 < qs; q2 += nwx) {
-      vocab_token_tile(qf + q2, a.nvt, a.ntb, vt2, tb2);
-      if (tb2 * BN < Ts) break;
-    }
-    const bool more = q2 < qs;
+    int vt2 = 0, tb2 = 0;
+    const bool more = next_tile(vt2, tb2);
     if (more) {
       weight_hidden_loaders<NW>(a.W, a.ldw, a.n_real, vt2 * BM, a.h, a.ldh, a.scored, tb2 * BN,
                                 Ts, a.H, la2, lb2);
@@ -417,7 +432,6 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
     dma::mainloop_chain(la, lb, la2, lb2, primed, more, n, smem, acc);
     fwd_tile_epilogue<NFB>(acc, a, vt, tb, Ts, red);
     if (!more) break;
-    q = q2;
     vt = vt2;
     tb = tb2;
     la = la2;

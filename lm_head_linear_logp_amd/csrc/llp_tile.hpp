@@ -71,32 +71,36 @@ __device__ __forceinline__ int queue_size(int n, int x) {
 }
 __device__ __forceinline__ int queue_static(int size) { return size - (size + 3) / 4; }
 
+// One dynamic tile of n for a workgroup on XCD x, or -1 when every queue's dynamic part is
+// empty: global atomic operations (vector memory) on ctr[0..8] (zero at the launch), own XCD's
+// queue first. Called by one thread.
+__device__ __forceinline__ int claim_dynamic(int* ctr, int n, int x) {
+  int t = -1;
+  int k = atomicAdd(ctr + x, 1);
+  if (k < queue_size(n, x) - queue_static(queue_size(n, x))) {
+    t = queue_first(n, x) + queue_static(queue_size(n, x)) + k;
+  } else if (atomicOr(ctr + NUM_XCD, 0) == 0) {
+    for (int d = 1; d < NUM_XCD && t < 0; ++d) {
+      const int y = (x + d) % NUM_XCD;
+      const int sy = queue_static(queue_size(n, y));
+      k = atomicAdd(ctr + y, 1);
+      if (k < queue_size(n, y) - sy) t = queue_first(n, y) + sy + k;
+    }
+    if (t < 0) atomicOr(ctr + NUM_XCD, 1);
+  }
+  return t;
+}
+
 // The workgroup's logical tile of n, or -1 when every queue is empty. Called by every thread
-// (the static branch is uniform). For a dynamic tile, thread 0 takes it with global atomic
-// operations (vector memory) on ctr[0..8] (zero at the launch), own XCD's queue first, and the
-// tile reaches the other threads through `slot`, a word of the pipeline's LDS (a separate
-// __shared__ word would take the workgroup past 128 KiB of LDS: for the 8-wave forward tile
-// 4 more bytes measured 62% slower).
+// (the static branch is uniform). A dynamic tile is claimed by thread 0 and reaches the other
+// threads through `slot`, a word of the pipeline's LDS (a separate __shared__ word would be a
+// second LDS object, and with two the compiler no longer tells the stages' DMA writes from
+// the fragment reads: it waits for every DMA load before each read, measured 62% slower).
 __device__ __forceinline__ int take_tile(int* ctr, int n, int* slot) {
   const int x = blockIdx.x % NUM_XCD, i = blockIdx.x / NUM_XCD;
   const int s0 = queue_static(queue_size(n, x));
   if (i < s0) return queue_first(n, x) + i;
-  if (threadIdx.x == 0) {
-    int t = -1;
-    int k = atomicAdd(ctr + x, 1);
-    if (k < queue_size(n, x) - s0) {
-      t = queue_first(n, x) + s0 + k;
-    } else if (atomicOr(ctr + NUM_XCD, 0) == 0) {
-      for (int d = 1; d < NUM_XCD && t < 0; ++d) {
-        const int y = (x + d) % NUM_XCD;
-        const int sy = queue_static(queue_size(n, y));
-        k = atomicAdd(ctr + y, 1);
-        if (k < queue_size(n, y) - sy) t = queue_first(n, y) + sy + k;
-      }
-      if (t < 0) atomicOr(ctr + NUM_XCD, 1);
-    }
-    *slot = t;
-  }
+  if (threadIdx.x == 0) *slot = claim_dynamic(ctr, n, x);
   __syncthreads();
   const int t = *slot;
   __syncthreads();   // the slot sits in the pipeline's LDS, which the first DMA overwrites

@@ -93,6 +93,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t) {
   extent(a.tz, Tc);
   extent(a.scored, Tc);
   extent(a.tloc, Tc);
+  extent(a.qctr, QCTR_INTS);
   return a.pstride >= Tc ? hipSuccess : hipErrorInvalidValue;
 }
 hipError_t launch_combine(const CombineArgs& a, int64_t T_cap, hipStream_t) {

@@ -82,6 +82,30 @@ def test_tiles_and_ragged_tails(llp, shape):
             assert bytes_equal(out[k], out32[k]), k
 
 
+# Over 256 tiles: the persistent forward workers (one per compute unit) run several tiles each,
+# chaining each tile's last K steps into the next tile's first loads. Two K steps (H = 128) is
+# the shortest chain; the masked case skips whole token blocks past the scored rows.
+MANY_TILES = [  # T, H, V_real, V_pad, tau, mask_frac, bias
+    (512, 128, 131000, 131072, 0.7, 0.0, False),
+    (700, 256, 99990, 100096, 0.9, 0.4, True),
+]
+
+
+@pytest.mark.parametrize("shape", MANY_TILES, ids=[f"T{s[0]}_H{s[1]}_V{s[2]}" for s in MANY_TILES])
+def test_several_tiles_per_worker(llp, shape):
+    T, H, Vr, Vp, tau, mf, hb = shape
+    case = synth.small_case(T, H, Vr, Vp, tau, case_id=90 + H, mask_frac=mf, with_bias=hb,
+                            w_std=0.05)
+    say(f"many-tile forward {shape}")
+    ref = oracle.forward(case["hidden"], case["weight"], case["bias"], tau, case["targets"],
+                         case["mask"], Vr)
+    out = run_forward(llp, case)
+    check_forward(out, ref, case["mask"], f"many{shape}")
+    again = run_forward(llp, case)
+    for k in ("logp", "entropy", "lse", "target_logit", "in_range"):
+        assert bytes_equal(out[k], again[k]), k
+
+
 def test_padded_columns_excluded_bitwise(llp):
     case = synth.small_case(200, 256, 700, 768, 0.7, case_id=40, w_std=0.05)
     a = run_forward(llp, case)
