@@ -343,8 +343,9 @@ __device__ __forceinline__ void weight_hidden_loaders(const uint16_t* W, int64_t
 }
 
 // The forward's LDS: the pipeline's two stages, then the epilogue's 6 x 256 fp32 partials and a
-// word for tile claims. One array, not several: with a second LDS object the compiler can no longer tell the stages' DMA
-// writes from the fragment reads and waits for every DMA load before each read.
+// word for tile claims. One array, not several: with a second LDS object the compiler can no
+// longer tell the stages' DMA writes from the fragment reads and waits for every DMA load
+// before each read.
 constexpr int FWD_LDS_HALFS = dma::LDS_BYTES / 2 + 6 * 256 * 2 + 8;   // + the tile-claim slot
 static_assert(dma::BKD == KSTEP, "K step shared with the host");
 static_assert(QCTR_INTS > NUM_XCD, "queue counters and the all-empty flag");
