@@ -232,7 +232,13 @@ using Loader = LoaderT<4>;
 // The resource is rebased at every K step (its base is that step's first row), so offsets stay
 // small for any number of rows; rows past `maxrow` (the last readable one) are read as maxrow
 // and columns past the valid ones as column 0 (callers never use those values).
-__device__ __forceinline__ int fk(int r) { return 2 * (r & 3); }
+// The swizzle spreads one transposing fragment read (FragOp<true>) over every LDS bank: its 64
+// lanes read 8 bytes each from K-rows 8(g/2) + j (g = lane/16, j = lane/4 % 4) at chunks
+// C + 2(g%2) + (lane/2 % 2), so XOR-ing the chunk with 4j + 16(g/2) gives the 64 lanes 64
+// distinct 8-byte slots of a 512-byte window: each of the 64 four-byte banks is read twice,
+// the minimum for 512 bytes. (XOR-ing with 2j alone left pairs of lanes on one bank in every
+// half-wave.)
+__device__ __forceinline__ int fk(int r) { return 4 * (r & 3) + 16 * ((r >> 3) & 1); }
 
 // One K-major DMA instruction (non-template, like BufRsrc): the resource is based at K step
 // `kstep`'s first row, 16 bytes per lane from byte offset voff into the LDS window at `lds`.
@@ -255,7 +261,7 @@ struct LoaderKT {
   int64_t ld;            // row stride (elements)
   int maxrow;            // last readable row
   int r0;                // this lane's K-row for u = 0 within a step: KR w + lane/32
-  int cb[2];             // byte offset of this lane's chunk within a K-row, by u parity
+  int cb[NIW];           // byte offset of this lane's source chunk for instruction u
 
   __device__ __forceinline__ void init(const uint16_t* b, int64_t ld_, int maxrow_, int ncols) {
     base = b;
@@ -264,17 +270,18 @@ struct LoaderKT {
     const int lane = threadIdx.x & 63;
     r0 = KR * (threadIdx.x >> 6) + (lane >> 5);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      int c = (lane & 31) ^ fk(2 * p + (lane >> 5));
+    for (int u = 0; u < NIW; ++u) {
+      // Position lane % 32 of the stage's K-row r0 + 2u holds chunk (lane % 32) ^ fk(r0 + 2u).
+      int c = (lane & 31) ^ fk(r0 + 2 * u);
       if (8 * c >= ncols) c = 0;
-      cb[p] = 16 * c;
+      cb[u] = 16 * c;
     }
   }
   __device__ __forceinline__ void issue1(uint16_t* stage, int kstep, int u) const {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rlim = maxrow - kstep * BKD;
     const int r = r0 + 2 * u < rlim ? r0 + 2 * u : rlim;
-    loadk_issue(base, ld, kstep, stage + (KR * w + 2 * u) * BM, (uint32_t)(r * (int)ld * 2 + cb[u & 1]));
+    loadk_issue(base, ld, kstep, stage + (KR * w + 2 * u) * BM, (uint32_t)(r * (int)ld * 2 + cb[u]));
   }
 };
 using LoaderK = LoaderKT<4>;
@@ -319,7 +326,8 @@ struct FragOp<true, NF> {
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
       const int chunk = wx * 4 * NF + 4 * i + 2 * (g & 1) + (t >> 1);
-      off[i] = (8 * (g >> 1) + j) * (BM * 2) + 16 * (chunk ^ (2 * j)) + 8 * (t & 1);
+      const int row = 8 * (g >> 1) + j;   // fk of every K-row this lane reads is fk(row)
+      off[i] = row * (BM * 2) + 16 * (chunk ^ fk(row)) + 8 * (t & 1);
     }
   }
   // K-rows 16kk + 8(g/2) + 4h .. +3 of this lane's column.
