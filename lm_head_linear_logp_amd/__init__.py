@@ -5,7 +5,8 @@ PyTorch supplies device memory (outputs, workspace) and the current HIP stream. 
 CPU fallback: if the library is missing or the device is not a gfx950 GPU, calls raise.
 
 Functions mirror the ABI: ``open``, ``workspace_bytes``, ``forward``, ``merge``, ``backward``,
-``top_p_replay``, ``last_error``.
+``top_p_replay``, ``last_error``. ``linear_logp`` composes ``forward`` and ``backward`` into
+one autograd node for a full-vocabulary shard.
 """
 from __future__ import annotations
 
@@ -18,7 +19,7 @@ from . import _capi as A
 
 __all__ = ["LLPError", "open", "workspace_bytes", "forward", "forward_noalloc", "merge",
            "backward", "top_p_replay", "last_error", "STATUS_BITS", "forward_logits",
-           "keep_mask_replay", "SCRATCH_BYTES"]
+           "keep_mask_replay", "SCRATCH_BYTES", "linear_logp"]
 
 # Size of the static device scratch llp_forward_noalloc works in (include/llp.h).
 SCRATCH_BYTES = 32 << 20
@@ -508,3 +509,57 @@ def keep_mask_replay(logits: torch.Tensor, keep_mask: torch.Tensor, target_ids: 
     _check(A.load().llp_keep_mask_replay(C.byref(req), C.byref(o), _stream_ptr(dev)),
            "llp_keep_mask_replay")
     return out
+
+
+class _LinearLogp(torch.autograd.Function):
+    """forward + backward of one full-vocabulary shard as an autograd node (world = 1)."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, bias, target_ids, loss_mask, temperature, real_vocab,
+                padded_vocab, want_entropy):
+        out = forward(hidden, weight, target_ids, temperature=temperature, bias=bias,
+                      loss_mask=loss_mask, real_vocab=real_vocab, padded_vocab=padded_vocab,
+                      want_entropy=want_entropy)
+        ctx.save_for_backward(hidden, weight, bias, target_ids, loss_mask, out["lse"],
+                              out["entropy"])
+        ctx.cfg = (temperature, real_vocab, padded_vocab)
+        ctx.mark_non_differentiable(out["lse"])
+        ent = out["entropy"] if want_entropy else out["lse"].new_zeros(0)
+        return out["logp"], ent, out["lse"]
+
+    @staticmethod
+    def backward(ctx, dlogp, dentropy, _dlse):
+        hidden, weight, bias, target_ids, loss_mask, lse, entropy = ctx.saved_tensors
+        temperature, real_vocab, padded_vocab = ctx.cfg
+        T = hidden.shape[0]
+        if dlogp is None:
+            dlogp = torch.zeros(T, dtype=torch.float32, device=hidden.device)
+        use_ent = dentropy is not None and entropy is not None and dentropy.numel() == T
+        g = backward(hidden, weight, target_ids, lse, dlogp.float().contiguous(),
+                     temperature=temperature, bias=bias, loss_mask=loss_mask,
+                     real_vocab=real_vocab, padded_vocab=padded_vocab,
+                     dentropy=dentropy.float().contiguous() if use_ent else None,
+                     entropy=entropy if use_ent else None, overwrite=True,
+                     want_dbias=bias is not None and ctx.needs_input_grad[2])
+        dW = g["dweight"].to(weight.dtype) if ctx.needs_input_grad[1] else None
+        db = g["dbias"].to(bias.dtype) if bias is not None and ctx.needs_input_grad[2] else None
+        dH = g["dhidden"] if ctx.needs_input_grad[0] else None
+        return dH, dW, db, None, None, None, None, None, None
+
+
+def linear_logp(hidden: torch.Tensor, weight: torch.Tensor, target_ids: torch.Tensor, *,
+                temperature: float, bias: Optional[torch.Tensor] = None,
+                loss_mask: Optional[torch.Tensor] = None, real_vocab: Optional[int] = None,
+                padded_vocab: Optional[int] = None, want_entropy: bool = True):
+    """Per-token log-probability of target_ids (and entropy) under softmax((h W^T + b) / tau)
+    over the real vocabulary, differentiable in hidden, weight and bias: the operator's
+    forward, and in autograd's backward pass its backward with the incoming dlogp/dentropy
+    ([CUDA provider, "Motivation"]: gradients must flow). One full-vocabulary shard (world = 1).
+    Returns (logp, entropy, lse); entropy is an empty tensor when want_entropy is False, and
+    lse carries no gradient. Rows with loss_mask 0 give logp = entropy = 0 and no gradient.
+    The weight and bias gradients are computed in fp32 and handed to autograd in the
+    parameters' dtype."""
+    if loss_mask is not None and loss_mask.dtype == torch.bool:
+        loss_mask = loss_mask.to(torch.uint8)
+    return _LinearLogp.apply(hidden, weight, bias, target_ids, loss_mask, temperature,
+                             real_vocab, padded_vocab, want_entropy)
