@@ -1,6 +1,8 @@
 """The execution calls under HIP graph capture ([CUDA provider, "Changes"]: the provider calls
 must be capturable into CUDA/HIP graphs). Forward + backward with caller-allocated outputs and
-workspace, and the forward in the library's static scratch, are captured once and replayed
+workspace, the forward in the library's static scratch, and the replay-side calls (compact
+replay over 4 shards and their merge, the logits-input forward, the dense keep-mask replay;
+their outputs allocated from the graph's pool during capture) are captured once and replayed
 several times. Between replays the program does its own eager work, overwrites the graph's
 outputs with NaN and synchronizes. Every replay must give bitwise the eager results (the
 workspace's tile-queue counters are zeroed by a kernel of the call, not by a memset node).
@@ -131,3 +133,74 @@ def test_noalloc_forward_replays_match_eager(llp):
         torch.cuda.synchronize()
         for k, v in ref.items():
             assert bytes_equal(fo[k], v), (rep, k)
+
+
+def _replay_inputs(seed):
+    g = np.random.default_rng(seed)
+    Tr, V, Vp = 300, 600, 640
+    x = (g.standard_normal((Tr, Vp)) * 2.0).astype(np.float32)
+    x[:, V:] = -1e30
+    ids = np.full((Tr, 64), -1, dtype=np.int64)
+    for t in range(Tr):
+        n = int(g.integers(0, 40))
+        lst = g.choice(V, size=n, replace=False)
+        lst = np.concatenate([lst, lst[: int(g.integers(0, n + 1))]])[:64]
+        g.shuffle(lst)
+        ids[t, :lst.size] = lst
+    tg = np.where(g.random(Tr) < 0.8, np.maximum(ids[:, 0], 0), g.integers(0, V, Tr))
+    keep = np.zeros((Tr, Vp), dtype=np.uint8)
+    for t in range(Tr):
+        keep[t, ids[t][ids[t] >= 0]] = 1
+    mask = (g.random(Tr) > 0.1).astype(np.uint8)
+    return dict(x=dev(x), ids=dev(ids), tg=dev(tg.astype(np.int64)), keep=dev(keep),
+                mask=dev(mask), V=V, Vp=Vp)
+
+
+def _replay_calls(llp, d):
+    """The replay-side execution calls: compact replay over 4 shards and their merge, the
+    logits-input forward and the dense keep-mask replay. Outputs come from the calls."""
+    V, Vp = d["V"], d["Vp"]
+    parts = []
+    for r, lo in enumerate(range(0, Vp, Vp // 4)):
+        hi = lo + Vp // 4
+        parts.append(llp.top_p_replay(d["x"][:, lo:hi], d["ids"], d["tg"], temperature=0.7,
+                                      offset=lo, real_vocab=V, padded_vocab=Vp, rank=r,
+                                      world=4, local_size=hi - lo, loss_mask=d["mask"]))
+    mg = llp.merge(parts, loss_mask=d["mask"], want_entropy=False)
+    fl = llp.forward_logits(d["x"], d["tg"], temperature=0.7, real_vocab=V, padded_vocab=Vp,
+                            loss_mask=d["mask"])
+    km = llp.keep_mask_replay(d["x"], d["keep"], d["tg"], temperature=0.7, real_vocab=V,
+                              padded_vocab=Vp, loss_mask=d["mask"])
+    outs = {f"merge.{k}": v for k, v in mg.items() if v is not None}
+    outs.update({f"logits.{k}": v for k, v in fl.items() if v is not None})
+    outs.update({f"keep.{k}": v for k, v in km.items() if v is not None})
+    return outs
+
+
+def test_replay_paths_replays_match_eager(llp):
+    d = _replay_inputs(7)
+    say("graph: eager replay paths")
+    ref = {k: v.clone() for k, v in _replay_calls(llp, d).items()}
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _replay_calls(llp, d)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("graph: capture replay paths")
+    with torch.cuda.graph(g):
+        outs = _replay_calls(llp, d)
+    torch.cuda.synchronize()
+    other = _replay_inputs(8)
+    for rep in range(4):
+        say(f"graph: replay-path replay {rep}")
+        _replay_calls(llp, other)
+        for v in outs.values():
+            v.fill_(7) if v.dtype == torch.uint8 else v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            assert bytes_equal(outs[k], v), (rep, k)
