@@ -1,0 +1,148 @@
+"""GPU parity at the largest sizes the C ABI accepts, where 32-bit address arithmetic would
+break first.
+
+- The fused forward and backward gather scored hidden rows through one buffer resource per tile
+  with 32-bit byte offsets from the tile's first scored row, so the host refuses hidden rows
+  that span 2^31 bytes or more. Here T * H * 2 is one row short of 2^31 bytes (T = 2^22 - 1,
+  H = 256). 300 rows are scored, including the first and the last row. The first token block
+  therefore spans almost the whole range, and the last one ends at the final row. Every
+  unscored row holds NaN, so a load of a wrong row would show in the results.
+- The logits-input forward, the compact top-p replay and the dense keep-mask replay address a
+  row of logits with 64-bit arithmetic. Here the logits exceed 2^32 bytes (fp32 and bf16), so
+  the last rows lie past any 32-bit byte offset.
+
+Inputs come from the seeded generators and are tiled on the device. Sampled rows, including the
+first and the last ones, are compared with the oracle; the rest are checked through properties
+that hold at any size (zero outputs of unscored rows; dense replay bitwise equal to compact)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests._gpu import (GRAD_GUARD, GRAD_RTOL, LOGP_ATOL, LOGP_GUARD, assert_rows_close, dev,
+                        dev_bf16, host, need_gpu, normwise_rel, record, say)
+
+pytestmark = pytest.mark.gpu
+
+BF16_NAN = 0x7FC0
+
+
+@pytest.fixture(scope="module")
+def llp():
+    need_gpu()
+    import lm_head_linear_logp_amd as m
+    m.open(0)
+    return m
+
+
+def test_fused_forward_backward_at_the_hidden_span_limit(llp):
+    H, Vr, Vp, tau, NS = 256, 1000, 1024, 0.7, 300
+    T = (1 << 31) // (2 * H) - 1                      # T * H * 2 = 2^31 - 512 bytes
+    case = synth.small_case(NS, H, Vr, Vp, tau, case_id=80, w_std=0.1)
+    g = synth.rng(1080, 9)
+    rows = np.sort(np.concatenate([[0, T - 1], g.choice(np.arange(1, T - 1), NS - 2,
+                                                         replace=False)]))
+    say(f"hidden span limit: T={T} H={H} ({T * H * 2} bytes), {NS} scored rows")
+    rows_d = dev(rows)
+    hidden = torch.full((T, H), BF16_NAN, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    hidden[rows_d] = dev_bf16(case["hidden"])
+    weight = dev_bf16(case["weight"])
+    tg = torch.zeros(T, dtype=torch.int64, device="cuda")
+    tg[rows_d] = dev(case["targets"])
+    mask = torch.zeros(T, dtype=torch.uint8, device="cuda")
+    mask[rows_d] = 1
+    unscored = mask == 0
+
+    out = llp.forward(hidden, weight, tg, temperature=tau, loss_mask=mask, real_vocab=Vr,
+                      padded_vocab=Vp)
+    torch.cuda.synchronize()
+    f = oracle.forward(case["hidden"], case["weight"], None, tau, case["targets"], None, Vr)
+    err = 0.0
+    for k in ("logp", "entropy", "lse"):
+        err = max(err, assert_rows_close(host(out[k][rows_d]), f[k], LOGP_ATOL, f"limit {k}"))
+        assert not bool(torch.any(out[k][unscored] != 0)), f"unscored rows of {k} are not 0"
+    np.testing.assert_array_equal(host(out["in_range"][rows_d]), f["in_range"])
+    record("hidden span limit: forward max |d|", err)
+    assert err <= LOGP_GUARD
+
+    dlogp = g.standard_normal(NS)
+    lse = torch.zeros(T, dtype=torch.float32, device="cuda")
+    lse[rows_d] = dev(f["lse"], torch.float32)
+    dl = torch.zeros(T, dtype=torch.float32, device="cuda")
+    dl[rows_d] = dev(dlogp, torch.float32)
+    b = llp.backward(hidden, weight, tg, lse, dl, temperature=tau, loss_mask=mask,
+                     real_vocab=Vr, padded_vocab=Vp, overwrite=True)
+    torch.cuda.synchronize()
+    ref = oracle.backward(case["hidden"], case["weight"], None, tau, case["targets"], None, 0,
+                          Vp, Vr, f["lse"], dlogp)
+    r1 = normwise_rel(oracle.bf16_to_f64(host(b["dhidden"][rows_d])), ref["dhidden"])
+    r2 = normwise_rel(host(b["dweight"]), ref["dweight"])
+    record("hidden span limit: dhidden normwise", r1)
+    record("hidden span limit: dweight normwise", r2)
+    assert r1 <= GRAD_RTOL and r2 <= GRAD_RTOL
+    assert r1 <= GRAD_GUARD and r2 <= GRAD_GUARD
+    dh_bits = b["dhidden"].view(torch.int16)
+    assert not bool(torch.any(dh_bits[unscored] != 0)), "unscored dhidden rows are not 0"
+    assert not bool(torch.any(b["dweight"][Vr:] != 0)), "padded dweight rows are not 0"
+
+
+REPLAY_LIMIT = [  # logits dtype, rows (T * 151936 * element size > 2^32 bytes)
+    (torch.float32, 8197),
+    (torch.bfloat16, 16389),
+]
+
+
+@pytest.mark.parametrize("dtype,T", REPLAY_LIMIT, ids=["f32", "bf16"])
+def test_logits_input_paths_past_4gib(llp, dtype, T):
+    Vr, Vp, tau, NB = synth.V_REAL_FULL, synth.V_PAD_FULL, 0.7, 16
+    esize = 4 if dtype == torch.float32 else 2
+    assert (T - 1) * Vp * esize > (1 << 32)
+    g = synth.rng(1081, 1 if dtype == torch.float32 else 2)
+    base = (g.standard_normal((NB, Vp)) * 2.0).astype(np.float32)
+    base[:, Vr:] = np.float32(1e30)                    # padded columns: never part of a row
+    ids = np.full((NB, 64), -1, dtype=np.int64)
+    keep = np.zeros((NB, Vp), dtype=np.uint8)
+    member = np.zeros(NB, dtype=np.int64)
+    for r in range(NB):
+        u = g.choice(Vr, 1 + r, replace=False)          # 1..16 distinct ids per row
+        ids[r, g.choice(64, u.size, replace=False)] = u
+        keep[r, u] = 1
+        member[r] = u[0]
+    idx = np.arange(T) % NB
+    # Half the targets lie in their row's nucleus, the others anywhere in the real vocabulary.
+    tg = np.where(g.random(T) < 0.5, member[idx], g.integers(0, Vr, T)).astype(np.int64)
+    mask = (g.random(T) >= 0.1).astype(np.uint8)
+    mask[[0, T - 1]] = 1
+    say(f"logits past 4 GiB: T={T} {dtype} ({T * Vp * esize} bytes)")
+
+    bd = dev(base)
+    if dtype == torch.bfloat16:
+        bd = bd.to(torch.bfloat16)
+    vals = bd.float().cpu().numpy().astype(np.float64)  # the exact values the kernels read
+    idx_d = dev(idx)
+    X = bd[idx_d]
+    K = dev(keep)[idx_d]
+    I, G, M = dev(ids[idx]), dev(tg), dev(mask)
+    kw = dict(temperature=tau, real_vocab=Vr, padded_vocab=Vp, loss_mask=M)
+    fl = llp.forward_logits(X, G, want_entropy=True, **kw)
+    tp = llp.top_p_replay(X, I, G, **kw)
+    km = llp.keep_mask_replay(X, K, G, **kw)
+    torch.cuda.synchronize()
+
+    for k in ("target_logit", "in_range", "lse", "logp"):
+        assert torch.equal(tp[k], km[k]), f"dense and compact replay differ in {k}"
+    rows = np.unique(np.concatenate([[0, 1, 2, T - 3, T - 2, T - 1],
+                                     g.integers(0, T, 20)]))
+    rf = oracle.logits_forward(vals[idx[rows]], tg[rows], tau, 0, Vp, Vr, mask[rows])
+    rt = oracle.top_p_replay(vals[idx[rows]], ids[idx[rows]], tg[rows], tau, 0, Vp, Vr,
+                             mask[rows])
+    err = 0.0
+    for k in ("lse", "logp", "entropy"):
+        err = max(err, assert_rows_close(host(fl[k])[rows], rf[k], LOGP_ATOL, f"logits {k}"))
+    for k in ("lse", "logp"):
+        err = max(err, assert_rows_close(host(tp[k])[rows], rt[k], LOGP_ATOL, f"top-p {k}"))
+    np.testing.assert_array_equal(host(fl["in_range"])[rows], rf["in_range"])
+    np.testing.assert_array_equal(host(tp["in_range"])[rows], rt["in_range"])
+    record(f"logits past 4 GiB ({str(dtype)[6:]}): max |d|", err)
+    assert err <= LOGP_GUARD
