@@ -7,6 +7,11 @@ break first.
   H = 256). 300 rows are scored, including the first and the last row. The first token block
   therefore spans almost the whole range, and the last one ends at the final row. Every
   unscored row holds NaN, so a load of a wrong row would show in the results.
+- A shard's local vocabulary may hold up to 2^23 - 256 columns. At that width the dhidden
+  product's buffer resource over 256 rows of G (all of its K range) just fits in 32 bits: it
+  ends 131088 bytes short of 2^32. Here the shard has exactly that width (H = 128, an fp32 bias,
+  the last 100 columns padding), and it is checked against the oracle evaluated window by
+  window.
 - The logits-input forward, the compact top-p replay and the dense keep-mask replay address a
   row of logits with 64-bit arithmetic. Here the logits exceed 2^32 bytes (fp32 and bf16), so
   the last rows lie past any 32-bit byte offset.
@@ -85,6 +90,62 @@ def test_fused_forward_backward_at_the_hidden_span_limit(llp):
     dh_bits = b["dhidden"].view(torch.int16)
     assert not bool(torch.any(dh_bits[unscored] != 0)), "unscored dhidden rows are not 0"
     assert not bool(torch.any(b["dweight"][Vr:] != 0)), "padded dweight rows are not 0"
+
+
+def test_vocabulary_at_the_local_size_limit(llp):
+    Vp = (1 << 23) - 256                               # local_size = padded vocabulary
+    Vr, H, T, tau, P = Vp - 100, 128, 8, 0.7, 65521
+    # Weight and bias rows repeat with a prime period: a row read from a wrapped 32-bit
+    # offset (a multiple of 2^24 rows away) would hold other values.
+    g = synth.rng(1082, 1)
+    wb = synth.normal_bf16(g, (P, H), 0.1)
+    bb = (g.standard_normal(P) * 0.5).astype(np.float32)
+    hid = synth.normal_bf16(g, (T, H), 1.0)
+    tg = np.concatenate([[0, Vr - 1, Vp - 101 - 7, P, 2 * P + 5],
+                         g.integers(0, Vr, T - 5)]).astype(np.int64)
+    say(f"local size limit: V={Vp} ({Vr} real) H={H} T={T}")
+    idx_d = dev(np.arange(Vp, dtype=np.int64) % P)
+    W = dev_bf16(wb)[idx_d]
+    bias = dev(bb)[idx_d]
+    out = llp.forward(dev_bf16(hid), W, dev(tg), temperature=tau, bias=bias, real_vocab=Vr,
+                      padded_vocab=Vp)
+    torch.cuda.synchronize()
+
+    # The oracle over windows of the vocabulary (shards of one call), merged in order.
+    step = 1 << 20
+    wins = [(lo, min(lo + step, Vp)) for lo in range(0, Vp, step)]
+    rows_of = lambda lo, hi: np.arange(lo, hi) % P
+    parts = [oracle.shard_forward(hid, wb[rows_of(lo, hi)], bb[rows_of(lo, hi)], tau, tg, None,
+                                  lo, hi - lo, Vr) for lo, hi in wins]
+    f = oracle.merge(parts)
+    err = 0.0
+    for k in ("logp", "entropy", "lse"):
+        err = max(err, assert_rows_close(host(out[k]), f[k], LOGP_ATOL, f"local size limit {k}"))
+    record("local size limit: forward max |d|", err)
+    assert err <= LOGP_GUARD
+
+    dlogp = g.standard_normal(T)
+    b = llp.backward(dev_bf16(hid), W, dev(tg), dev(f["lse"], torch.float32),
+                     dev(dlogp, torch.float32), temperature=tau, bias=bias, real_vocab=Vr,
+                     padded_vocab=Vp, overwrite=True)
+    torch.cuda.synchronize()
+    dH = np.zeros((T, H))
+    checked = {0, len(wins) // 2, len(wins) - 1}
+    for i, (lo, hi) in enumerate(wins):
+        r = rows_of(lo, hi)
+        ref = oracle.backward(hid, wb[r], bb[r], tau, tg, None, lo, hi - lo, Vr, f["lse"], dlogp)
+        dH += ref["dhidden"]
+        if i in checked:
+            rw = normwise_rel(host(b["dweight"][lo:hi]), ref["dweight"])
+            rb = normwise_rel(host(b["dbias"][lo:hi]), ref["dbias"])
+            record(f"local size limit: dweight rows [{lo}, {hi}) normwise", rw)
+            record(f"local size limit: dbias [{lo}, {hi}) normwise", rb)
+            assert rw <= GRAD_GUARD and rb <= GRAD_GUARD
+    rh = normwise_rel(oracle.bf16_to_f64(host(b["dhidden"])), dH)
+    record("local size limit: dhidden normwise", rh)
+    assert rh <= GRAD_GUARD
+    assert not bool(torch.any(b["dweight"][Vr:] != 0)), "padded dweight rows are not 0"
+    assert not bool(torch.any(b["dbias"][Vr:] != 0)), "padded dbias entries are not 0"
 
 
 REPLAY_LIMIT = [  # logits dtype, rows (T * 151936 * element size > 2^32 bytes)
