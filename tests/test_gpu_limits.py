@@ -12,6 +12,9 @@ break first.
   ends 131088 bytes short of 2^32. Here the shard has exactly that width (H = 128, an fp32 bias,
   the last 100 columns padding), and it is checked against the oracle evaluated window by
   window.
+- The hidden size may be up to 2^20. At that size a tile's K loop runs 16384 steps, the
+  dhidden and dweight products span 4096 column tiles, and a dweight tile's rows are 4 MiB
+  apart. Here H = 2^20, with a bf16 bias and a ragged second vocabulary tile.
 - The logits-input forward, the compact top-p replay and the dense keep-mask replay address a
   row of logits with 64-bit arithmetic. Here the logits exceed 2^32 bytes (fp32 and bf16), so
   the last rows lie past any 32-bit byte offset.
@@ -146,6 +149,42 @@ def test_vocabulary_at_the_local_size_limit(llp):
     assert rh <= GRAD_GUARD
     assert not bool(torch.any(b["dweight"][Vr:] != 0)), "padded dweight rows are not 0"
     assert not bool(torch.any(b["dbias"][Vr:] != 0)), "padded dbias entries are not 0"
+
+
+def test_hidden_size_at_its_limit(llp):
+    H, T, Vr, Vp, tau = 1 << 20, 8, 300, 320, 0.7
+    case = synth.small_case(T, H, Vr, Vp, tau, case_id=83, mask_frac=0.2, with_bias=True,
+                            w_std=0.002)
+    say(f"hidden size limit: H={H} T={T} V={Vr}/{Vp}")
+    hid, W, bias = dev_bf16(case["hidden"]), dev_bf16(case["weight"]), dev_bf16(case["bias"])
+    tg, mask = dev(case["targets"]), dev(case["mask"])
+    out = llp.forward(hid, W, tg, temperature=tau, bias=bias, loss_mask=mask, real_vocab=Vr,
+                      padded_vocab=Vp)
+    torch.cuda.synchronize()
+    f = oracle.forward(case["hidden"], case["weight"], case["bias"], tau, case["targets"],
+                       case["mask"], Vr)
+    err = 0.0
+    for k in ("logp", "entropy", "lse"):
+        err = max(err, assert_rows_close(host(out[k]), f[k], LOGP_ATOL, f"hidden size limit {k}"))
+    record("hidden size limit: forward max |d|", err)
+    assert err <= LOGP_GUARD        # observed 5.5e-5: fp32 sums of 2^20 products
+
+    dlogp = synth.rng(1083, 5).standard_normal(T) * case["mask"]
+    b = llp.backward(hid, W, tg, dev(f["lse"], torch.float32), dev(dlogp, torch.float32),
+                     temperature=tau, bias=bias, loss_mask=mask, real_vocab=Vr, padded_vocab=Vp,
+                     overwrite=True)
+    torch.cuda.synchronize()
+    ref = oracle.backward(case["hidden"], case["weight"], case["bias"], tau, case["targets"],
+                          case["mask"], 0, Vp, Vr, f["lse"], dlogp)
+    dH = oracle.bf16_to_f64(host(b["dhidden"]))
+    r1 = normwise_rel(dH, ref["dhidden"])
+    r2 = normwise_rel(host(b["dweight"]), ref["dweight"])
+    r3 = normwise_rel(host(b["dbias"]), ref["dbias"])
+    for name, v in (("dhidden", r1), ("dweight", r2), ("dbias", r3)):
+        record(f"hidden size limit: {name} normwise", v)
+        assert v <= GRAD_GUARD
+    assert np.all(dH[case["mask"] == 0] == 0)
+    assert not bool(torch.any(b["dweight"][Vr:] != 0)), "padded dweight rows are not 0"
 
 
 REPLAY_LIMIT = [  # logits dtype, rows (T * 151936 * element size > 2^32 bytes)
