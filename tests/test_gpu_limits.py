@@ -15,6 +15,9 @@ break first.
 - The hidden size may be up to 2^20. At that size a tile's K loop runs 16384 steps, the
   dhidden and dweight products span 4096 column tiles, and a dweight tile's rows are 4 MiB
   apart. Here H = 2^20, with a bf16 bias and a ragged second vocabulary tile.
+- The merge takes up to 64 shards. Here 64 shards of seeded, uneven widths (some empty, some
+  padding only) are merged and compared with the unsharded oracle. Their backward calls with
+  the merged lse assemble the unsharded gradients.
 - The logits-input forward, the compact top-p replay and the dense keep-mask replay address a
   row of logits with 64-bit arithmetic. Here the logits exceed 2^32 bytes (fp32 and bf16), so
   the last rows lie past any 32-bit byte offset.
@@ -28,6 +31,7 @@ import torch
 
 import oracle
 import synth
+from lm_head_linear_logp_amd import _capi as A
 from tests._gpu import (GRAD_GUARD, GRAD_RTOL, LOGP_ATOL, LOGP_GUARD, assert_rows_close, dev,
                         dev_bf16, host, need_gpu, normwise_rel, record, say)
 
@@ -185,6 +189,52 @@ def test_hidden_size_at_its_limit(llp):
         assert v <= GRAD_GUARD
     assert np.all(dH[case["mask"] == 0] == 0)
     assert not bool(torch.any(b["dweight"][Vr:] != 0)), "padded dweight rows are not 0"
+
+
+def test_merge_of_the_largest_world(llp):
+    world = A.LLP_MAX_WORLD
+    T, H, Vr, Vp, tau = 300, 128, 16000, 16384, 0.7
+    case = synth.small_case(T, H, Vr, Vp, tau, case_id=84, mask_frac=0.2, w_std=0.1)
+    g = synth.rng(1084, 1)
+    # Seeded cut points, plus an empty shard at 5000 and a shard of padding only.
+    cuts = np.concatenate([[0], g.choice(Vp + 1, world - 5, replace=True),
+                           [5000, 5000, Vr, Vr + 100, Vp]])
+    cuts.sort()
+    widths = np.diff(cuts)
+    say(f"merge of {world} shards: {int((widths == 0).sum())} empty, widths up to {widths.max()}")
+    hid, tg, mk = dev_bf16(case["hidden"]), dev(case["targets"]), dev(case["mask"])
+    W = dev_bf16(case["weight"])
+    kw = dict(temperature=tau, loss_mask=mk, real_vocab=Vr, padded_vocab=Vp, world=world)
+    parts = [llp.forward(hid, W[lo:hi], tg, offset=int(lo), rank=r, **kw)
+             for r, (lo, hi) in enumerate(zip(cuts[:-1], cuts[1:]))]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mg = llp.merge(parts, loss_mask=mk, status=st)
+    torch.cuda.synchronize()
+    ref = oracle.forward(case["hidden"], case["weight"], None, tau, case["targets"], case["mask"],
+                         Vr)
+    err = 0.0
+    for k in ("logp", "lse", "entropy"):
+        err = max(err, assert_rows_close(host(mg[k]), ref[k], LOGP_ATOL, f"merged {k}"))
+    assert int(st.item()) == 0
+    record(f"merge of {world} shards: max |d|", err)
+    assert err <= LOGP_GUARD
+
+    dlogp = g.standard_normal(T) * case["mask"]
+    lse_d, dl_d = dev(ref["lse"], torch.float32), dev(dlogp, torch.float32)
+    dW = torch.empty((Vp, H), dtype=torch.float32, device="cuda")
+    dH = np.zeros((T, H))
+    for r, (lo, hi) in enumerate(zip(cuts[:-1], cuts[1:])):
+        b = llp.backward(hid, W[lo:hi], tg, lse_d, dl_d, offset=int(lo), rank=r,
+                         dweight=dW[lo:hi], overwrite=True, **kw)
+        dH += oracle.bf16_to_f64(host(b["dhidden"]))
+    torch.cuda.synchronize()
+    gref = oracle.backward(case["hidden"], case["weight"], None, tau, case["targets"],
+                           case["mask"], 0, Vp, Vr, ref["lse"], dlogp)
+    r1 = normwise_rel(dH, gref["dhidden"])
+    r2 = normwise_rel(host(dW), gref["dweight"])
+    record(f"{world} shards: summed dhidden normwise", r1)
+    record(f"{world} shards: assembled dweight normwise", r2)
+    assert r1 <= GRAD_RTOL and r2 <= GRAD_GUARD
 
 
 REPLAY_LIMIT = [  # logits dtype, rows (T * 151936 * element size > 2^32 bytes)
