@@ -105,10 +105,10 @@ typedef struct {
  *           shard's real columns (padding) are never read into a result.
  *   bias    [local_size] of bias_dtype (LLP_DTYPE_BF16 or LLP_DTYPE_F32), or NULL; 16-byte
  *           aligned base for F32, 8-byte for BF16.
- *   H must be a positive multiple of 64 (else LLP_ERR_UNSUPPORTED). Operand rows are addressed
- *   with 32-bit byte offsets, which bounds the envelope (else LLP_ERR_UNSUPPORTED):
- *   hidden_stride and weight_stride < 2^23, T * hidden_stride * 2 < 2^31 (the bytes the T
- *   hidden rows span), T <= 2^23 - 256 and local_size <= 2^23 - 256. */
+ *   H must be a positive multiple of 64, at most 2^20 (else LLP_ERR_UNSUPPORTED). Operand
+ *   rows are addressed with 32-bit byte offsets, which bounds the envelope (else
+ *   LLP_ERR_UNSUPPORTED): hidden_stride and weight_stride < 2^23, T * hidden_stride * 2 < 2^31
+ *   (the bytes the T hidden rows span), T <= 2^23 - 256 and local_size <= 2^23 - 256. */
 typedef struct {
   const void* hidden;
   int64_t hidden_stride;

@@ -151,6 +151,13 @@ BAD_FORWARD = [
     ("hidden bytes > 4 GiB", lambda r: (setattr(r.layout, "num_tokens", 1 << 20),
                                         setattr(r.proj, "hidden_stride", 4096)), A.LLP_ERR_UNSUPPORTED),
     ("weight stride >= 2^23", lambda r: setattr(r.proj, "weight_stride", 1 << 23), A.LLP_ERR_UNSUPPORTED),
+    ("H > 2^20", lambda r: (setattr(r.layout, "num_tokens", 8),
+                            setattr(r.proj, "hidden_size", (1 << 20) + 64),
+                            setattr(r.proj, "hidden_stride", (1 << 20) + 64),
+                            setattr(r.proj, "weight_stride", (1 << 20) + 64)), A.LLP_ERR_UNSUPPORTED),
+    ("local size 2^23 - 192", lambda r: (setattr(r.vocab, "padded_vocab", (1 << 23) - 192),
+                                         setattr(r.vocab, "local_size", (1 << 23) - 192),
+                                         setattr(r.vocab, "real_vocab", 1000)), A.LLP_ERR_UNSUPPORTED),
     ("shard too large", lambda r: (setattr(r.vocab, "padded_vocab", 1 << 24), setattr(r.vocab, "local_size", 1 << 24),
                                    setattr(r.vocab, "real_vocab", 1 << 24)), A.LLP_ERR_UNSUPPORTED),
     ("f32 bias misaligned", lambda r: (setattr(r.proj, "bias", FAKE + 8),
@@ -188,6 +195,23 @@ def test_valid_request_passes_validation():
     """A well-formed request gets past validation; without a device it fails afterwards."""
     st = call_forward(good_request())
     assert st not in (A.LLP_OK, A.LLP_ERR_INVALID_ARGUMENT) or "llp_open" in A.load().llp_last_error().decode()
+
+
+def test_requests_at_the_limits_pass_validation():
+    """H = 2^20 and a local vocabulary of 2^23 - 256 columns are inside the envelope: such
+    requests get past validation (one column or one 64-column step more is refused above)."""
+    def at_h_limit(r):
+        r.layout.num_tokens = 8
+        r.proj.hidden_size = r.proj.hidden_stride = r.proj.weight_stride = 1 << 20
+
+    def at_local_size_limit(r):
+        r.vocab.padded_vocab = r.vocab.local_size = (1 << 23) - 256
+        r.vocab.real_vocab = 1000
+
+    for fn in (at_h_limit, at_local_size_limit):
+        st = call_forward(_mut(fn))
+        assert st not in (A.LLP_ERR_INVALID_ARGUMENT, A.LLP_ERR_UNSUPPORTED), \
+            A.load().llp_last_error()
 
 
 def _ws_status(T, stride):
