@@ -80,8 +80,19 @@ enum { LLP_OP_FORWARD = 1, LLP_OP_BACKWARD = 2 };
  *   LLP_FLAG_OVERWRITE_GRADS  llp_backward writes dweight and dbias (= this call's gradient,
  *                             padding rows 0) instead of adding to them: the first chunk of a
  *                             step needs no zeroed buffer and no read of one. Ignored by
+ *                             llp_forward.
+ *   LLP_FLAG_G_SLABS          llp_backward never holds the whole G: it computes G, its
+ *                             dhidden and dweight products one vocabulary slab of
+ *                             LLP_G_SLAB_COLUMNS local columns at a time, in slab order, and
+ *                             adds each slab's dhidden into fp32 partials in the workspace.
+ *                             The workspace holds one slab of G instead of all of it
+ *                             (llp_workspace_bytes sizes it from this flag). dweight and dbias
+ *                             are bitwise those of the default mode; dhidden agrees to rounding
+ *                             (its vocabulary sum runs slab by slab) and is still bitwise
+ *                             reproducible and independent of the batch. Ignored by
  *                             llp_forward. */
-enum { LLP_FLAG_WANT_ENTROPY = 1, LLP_FLAG_OVERWRITE_GRADS = 2 };
+enum { LLP_FLAG_WANT_ENTROPY = 1, LLP_FLAG_OVERWRITE_GRADS = 2, LLP_FLAG_G_SLABS = 4 };
+#define LLP_G_SLAB_COLUMNS 32768
 
 /* Library identity and route evidence ([CUDA provider, "Changes"]: validation of identity;
  * native/provider route evidence). */
@@ -160,7 +171,7 @@ typedef struct {
  *   temperature  finite, > 0. Logits are z = (hidden . weight^T + bias) * fl32(1/temperature):
  *                temperature is applied exactly once ([ROCm provider, "Megatron
  *                integration"]; [top-p replay, "Summary"]).
- *   flags        LLP_FLAG_WANT_ENTROPY, LLP_FLAG_OVERWRITE_GRADS.
+ *   flags        LLP_FLAG_WANT_ENTROPY, LLP_FLAG_OVERWRITE_GRADS, LLP_FLAG_G_SLABS.
  *   status_word  int32 device word OR-ed with LLP_STATUS_* bits, or NULL. */
 typedef struct {
   llp_projection proj;

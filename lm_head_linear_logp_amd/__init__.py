@@ -291,15 +291,20 @@ def backward(hidden: torch.Tensor, weight: torch.Tensor, target_ids: torch.Tenso
              entropy: Optional[torch.Tensor] = None, dweight: Optional[torch.Tensor] = None,
              dbias: Optional[torch.Tensor] = None, want_dbias: Optional[bool] = None,
              dhidden: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None, overwrite: bool = False) -> dict:
+             workspace: Optional[torch.Tensor] = None, overwrite: bool = False,
+             g_slabs: bool = False) -> dict:
     """llp_backward on one shard: dhidden (bf16, overwritten), dweight (fp32, accumulated),
     dbias (fp32, accumulated; allocated when the request has a bias or want_dbias). With
     overwrite=True (LLP_FLAG_OVERWRITE_GRADS) dweight and dbias are written instead of added
-    to, and a missing dweight/dbias is allocated uninitialised."""
+    to, and a missing dweight/dbias is allocated uninitialised. With g_slabs=True
+    (LLP_FLAG_G_SLABS) the workspace holds G for one vocabulary slab of LLP_G_SLAB_COLUMNS
+    columns at a time instead of the whole shard."""
     req = _request(hidden, weight, target_ids, temperature, bias, loss_mask, cu_seqlens, offset,
                    real_vocab, padded_vocab, rank, world, False, status)
     if overwrite:
         req.flags |= A.LLP_FLAG_OVERWRITE_GRADS
+    if g_slabs:
+        req.flags |= A.LLP_FLAG_G_SLABS
     dev = hidden.device
     T, H = hidden.shape
     V = weight.shape[0]

@@ -24,6 +24,8 @@ LLP_OP_FORWARD = 1
 LLP_OP_BACKWARD = 2
 LLP_FLAG_WANT_ENTROPY = 1
 LLP_FLAG_OVERWRITE_GRADS = 2
+LLP_FLAG_G_SLABS = 4
+LLP_G_SLAB_COLUMNS = 32768
 LLP_MAX_REPLAY_IDS = 64
 LLP_MAX_WORLD = 64
 

@@ -114,7 +114,8 @@ llp_status check_request(const llp_request* req) {
   }
   LLP_CHECK(isfinite(req->temperature) && req->temperature > 0.f, LLP_ERR_INVALID_ARGUMENT,
             "temperature must be finite and > 0");
-  LLP_CHECK((req->flags & ~uint32_t(LLP_FLAG_WANT_ENTROPY | LLP_FLAG_OVERWRITE_GRADS)) == 0,
+  LLP_CHECK((req->flags & ~uint32_t(LLP_FLAG_WANT_ENTROPY | LLP_FLAG_OVERWRITE_GRADS |
+                                    LLP_FLAG_G_SLABS)) == 0,
             LLP_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", req->flags);
   if (req->layout.cu_seqlens != nullptr)
     LLP_CHECK(req->layout.num_seqs >= 0, LLP_ERR_INVALID_ARGUMENT, "num_seqs < 0");
@@ -125,13 +126,18 @@ llp_status check_request(const llp_request* req) {
 struct Ws {
   size_t count, qctr, scored, pos, tloc, tz, pm, ps, pq, G, hgT, P, dbp, total;
   int64_t T_cap, nvt, ldg;
+  int64_t slab_tiles, nslab;   // vocabulary tiles per slab of G and slabs per backward call
 };
 
-Ws ws_layout(int64_t T, int64_t n_real, int64_t H, int op) {
+// `slabs` (backward only): G is held one vocabulary slab of G_SLAB_TILES tiles at a time, so
+// its region (and the bias-gradient partials) take one slab's columns, ldg = the slab width.
+Ws ws_layout(int64_t T, int64_t n_real, int64_t H, int op, bool slabs = false) {
   Ws w{};
   w.T_cap = round_up(T > 0 ? T : 1, TILE);
   w.nvt = (n_real + TILE - 1) / TILE;
-  w.ldg = w.nvt * TILE;
+  w.slab_tiles = slabs && w.nvt > G_SLAB_TILES ? G_SLAB_TILES : (w.nvt > 0 ? w.nvt : 1);
+  w.nslab = w.nvt > 0 ? (w.nvt + w.slab_tiles - 1) / w.slab_tiles : 0;
+  w.ldg = w.slab_tiles * TILE;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -139,7 +145,8 @@ Ws ws_layout(int64_t T, int64_t n_real, int64_t H, int op) {
     return o;
   };
   w.count = take((size_t)(1 + layout_blocks(T)) * 4);   // 256 bytes up to 63 layout blocks
-  w.qctr = take(256);   // tile-queue counters: QCTR_INTS per GEMM kernel of the call
+  // Tile-queue counters: QCTR_INTS per GEMM kernel launch of the call (3 per slab backward).
+  w.qctr = take((size_t)(w.nslab > 1 ? 3 * w.nslab : 4) * QCTR_INTS * 4);
   w.scored = take((size_t)w.T_cap * 4);
   w.pos = take((size_t)w.T_cap * 4);
   w.tloc = take((size_t)w.T_cap * 4);
@@ -360,7 +367,8 @@ LLP_API llp_status llp_workspace_bytes(const llp_request* req, int32_t op, size_
   LLP_CHECK(op == LLP_OP_FORWARD || op == LLP_OP_BACKWARD, LLP_ERR_INVALID_ARGUMENT,
             "op %d is not LLP_OP_FORWARD or LLP_OP_BACKWARD", op);
   LLP_CHECK(bytes != nullptr, LLP_ERR_INVALID_ARGUMENT, "bytes is NULL");
-  *bytes = ws_layout(req->layout.num_tokens, local_real(req->vocab), req->proj.hidden_size, op).total;
+  *bytes = ws_layout(req->layout.num_tokens, local_real(req->vocab), req->proj.hidden_size, op,
+                     op == LLP_OP_BACKWARD && (req->flags & LLP_FLAG_G_SLABS) != 0).total;
   return LLP_OK;
 }
 
@@ -557,7 +565,7 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
     LLP_CHECK(out->dweight_stride < (int64_t(1) << 21), LLP_ERR_UNSUPPORTED,
               "dweight_stride must be < 2^21");
   }
-  const Ws w = ws_layout(T, n_real, H, LLP_OP_BACKWARD);
+  const Ws w = ws_layout(T, n_real, H, LLP_OP_BACKWARD, (req->flags & LLP_FLAG_G_SLABS) != 0);
   LLP_CHECK(workspace_bytes >= w.total, LLP_ERR_INVALID_ARGUMENT,
             "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, w.total);
   LLP_CHECK(workspace != nullptr && aligned(workspace, 256), LLP_ERR_INVALID_ARGUMENT,
@@ -600,9 +608,11 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
   la.pos = at<int32_t>(workspace, w.pos);
   la.tloc = at<int32_t>(workspace, w.tloc);
   la.status = req->status_word;
-  int32_t* qctr = at<int32_t>(workspace, w.qctr);   // gradient, dhidden, dweight counters
+  // Gradient, dhidden and dweight counters for each vocabulary slab (one slab unless
+  // LLP_FLAG_G_SLABS splits the shard's columns).
+  int32_t* qctr = at<int32_t>(workspace, w.qctr);
   la.qctr = qctr;
-  la.nqctr = 3 * QCTR_INTS;
+  la.nqctr = (int32_t)(3 * QCTR_INTS * (w.nslab > 0 ? w.nslab : 1));
   LLP_HIP(launch_layout(la, s), "layout kernel launch");
 
   const int ntb = (int)(w.T_cap / TILE);
@@ -622,73 +632,90 @@ LLP_API llp_status llp_backward(const llp_request* req, const llp_bwd_in* in,
     th.ldo = w.T_cap;
     LLP_HIP(launch_transpose(th, w.T_cap, s), "transpose kernel launch");
 
-    GradArgs ga{};
-    ga.W = static_cast<const uint16_t*>(req->proj.weight);
-    ga.ldw = req->proj.weight_stride;
-    ga.h = static_cast<const uint16_t*>(req->proj.hidden);
-    ga.ldh = req->proj.hidden_stride;
-    ga.bias = req->proj.bias;
-    ga.bias_f32 = req->proj.bias_dtype == LLP_DTYPE_F32;
-    ga.H = (int32_t)H;
-    ga.n_real = n_real;
-    ga.nvt = (int32_t)w.nvt;
-    ga.ntb = ntb;
-    ga.c1 = (float)(1.0 / (double)req->temperature);
-    ga.count = la.count;
-    ga.scored = la.scored;
-    ga.tloc = la.tloc;
-    ga.lse = in->lse;
-    ga.dlogp = in->dlogp;
-    ga.dent = in->dentropy;
-    ga.ent = in->entropy;
-    ga.G = G;
-    ga.ldg = w.ldg;
-    ga.qctr = qctr;
-    ga.dbp = out->dbias != nullptr ? at<float>(workspace, w.dbp) : nullptr;
+    // Vocabulary slabs in order (the whole shard is one slab by default). Each slab's G tiles
+    // are written to the workspace, then read by its dhidden product (added into the fp32
+    // partials after the first slab) and its dweight and dbias products, which write the
+    // slab's own rows.
+    const uint16_t* W = static_cast<const uint16_t*>(req->proj.weight);
+    const int64_t slab_cols = w.slab_tiles * TILE;
+    for (int64_t sl = 0; sl < w.nslab; ++sl) {
+      const int64_t v0 = sl * slab_cols;
+      const int64_t nr = n_real - v0 < slab_cols ? n_real - v0 : slab_cols;
+      const int32_t nvt = (int32_t)((nr + TILE - 1) / TILE);
+      int32_t* qs = qctr + 3 * QCTR_INTS * sl;
+
+      GradArgs ga{};
+      ga.W = W + v0 * req->proj.weight_stride;
+      ga.ldw = req->proj.weight_stride;
+      ga.h = static_cast<const uint16_t*>(req->proj.hidden);
+      ga.ldh = req->proj.hidden_stride;
+      ga.bias_f32 = req->proj.bias_dtype == LLP_DTYPE_F32;
+      ga.bias = req->proj.bias == nullptr ? nullptr
+                : ga.bias_f32 ? (const void*)(static_cast<const float*>(req->proj.bias) + v0)
+                              : (const void*)(static_cast<const uint16_t*>(req->proj.bias) + v0);
+      ga.H = (int32_t)H;
+      ga.n_real = nr;
+      ga.nvt = nvt;
+      ga.ntb = ntb;
+      ga.c1 = (float)(1.0 / (double)req->temperature);
+      ga.count = la.count;
+      ga.scored = la.scored;
+      ga.tloc = la.tloc;
+      ga.toff = (int32_t)v0;
+      ga.lse = in->lse;
+      ga.dlogp = in->dlogp;
+      ga.dent = in->dentropy;
+      ga.ent = in->entropy;
+      ga.G = G;
+      ga.ldg = w.ldg;
+      ga.qctr = qs;
+      ga.dbp = out->dbias != nullptr ? at<float>(workspace, w.dbp) : nullptr;
       LLP_HIP(launch_grad(ga, s), "gradient kernel launch");
 
-    DhArgs da{};
-    da.G = G;
-    da.ldg = w.ldg;
-    da.W = static_cast<const uint16_t*>(req->proj.weight);
-    da.ldw = req->proj.weight_stride;
-    da.n_real = n_real;
-    da.H = (int32_t)H;
-    da.ntm = ntb;
-    da.ntn = (int32_t)((H + TILE - 1) / TILE);
-    da.nsplit = DH_SPLITS;
-    da.nks = (int32_t)((n_real + KSTEP - 1) / KSTEP);
-    da.count = la.count;
-    da.P = P;
-    da.pstride = w.T_cap;
-    da.qctr = qctr + QCTR_INTS;
+      DhArgs da{};
+      da.G = G;
+      da.ldg = w.ldg;
+      da.W = ga.W;
+      da.ldw = req->proj.weight_stride;
+      da.n_real = nr;
+      da.H = (int32_t)H;
+      da.ntm = ntb;
+      da.ntn = (int32_t)((H + TILE - 1) / TILE);
+      da.nsplit = DH_SPLITS;
+      da.nks = (int32_t)((nr + KSTEP - 1) / KSTEP);
+      da.count = la.count;
+      da.P = P;
+      da.pstride = w.T_cap;
+      da.accumulate = sl > 0;
+      da.qctr = qs + QCTR_INTS;
       LLP_HIP(launch_dh(da, s), "dhidden kernel launch");
 
-    DwArgs wa{};
-    wa.G = G;
-    wa.ldg = w.ldg;
-    wa.hgT = hgT;
-    wa.ldk = w.T_cap;
-    wa.H = (int32_t)H;
-    wa.ntm = (int32_t)w.nvt;
-    wa.ntn = da.ntn;
-    wa.n_real = n_real;
-    wa.count = la.count;
-    wa.dW = out->dweight;
-    wa.lddw = out->dweight_stride;
-    wa.overwrite = overwrite;
-    wa.qctr = qctr + 2 * QCTR_INTS;
+      DwArgs wa{};
+      wa.G = G;
+      wa.ldg = w.ldg;
+      wa.hgT = hgT;
+      wa.ldk = w.T_cap;
+      wa.H = (int32_t)H;
+      wa.ntm = nvt;
+      wa.ntn = da.ntn;
+      wa.n_real = nr;
+      wa.count = la.count;
+      wa.dW = out->dweight + v0 * out->dweight_stride;
+      wa.lddw = out->dweight_stride;
+      wa.overwrite = overwrite;
+      wa.qctr = qs + 2 * QCTR_INTS;
       LLP_HIP(launch_dw(wa, s), "dweight kernel launch");
 
-    if (out->dbias != nullptr) {
-      DbArgs ba{};
-      ba.dbp = ga.dbp;
-      ba.ldp = w.ldg;
-      ba.n_real = n_real;
-      ba.count = la.count;
-      ba.db = out->dbias;
-      ba.overwrite = overwrite;
-      LLP_HIP(launch_dbias(ba, s), "dbias kernel launch");
+      if (out->dbias != nullptr) {
+        DbArgs ba{};
+        ba.dbp = ga.dbp;
+        ba.ldp = w.ldg;
+        ba.n_real = nr;
+        ba.count = la.count;
+        ba.db = out->dbias + v0;
+        ba.overwrite = overwrite;
+        LLP_HIP(launch_dbias(ba, s), "dbias kernel launch");
+      }
     }
   }
   DhReduceArgs ra{};

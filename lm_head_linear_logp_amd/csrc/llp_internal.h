@@ -19,6 +19,8 @@ constexpr size_t SCRATCH_BYTES = size_t(32) << 20;
 constexpr int MAX_DEVICES = 64;
 constexpr int KSTEP = 64;  // K depth of one pipelined GEMM step
 constexpr int QCTR_INTS = 16;  // tile-queue counters per GEMM kernel launch (llp_tile.hpp)
+// Vocabulary tiles per slab of G with LLP_FLAG_G_SLABS (LLP_G_SLAB_COLUMNS / TILE).
+constexpr int G_SLAB_TILES = LLP_G_SLAB_COLUMNS / 256;
 // Rows per workgroup of the layout scan when it takes several; up to that many rows one
 // workgroup scans them all.
 constexpr int64_t LAYOUT_BLOCK_ROWS = 16384;
@@ -45,7 +47,7 @@ struct LayoutArgs {
   float* out_p;
   int32_t* status;
   int32_t* qctr;    // tile-queue counters of the GEMM kernels of this call, zeroed here
-  int32_t nqctr;    // (at most 1024)
+  int32_t nqctr;
 };
 
 struct FwdArgs {
@@ -173,6 +175,7 @@ struct GradArgs {
   const int32_t* count;
   const int32_t* scored;
   const int32_t* tloc;
+  int32_t toff;     // local column of the weight's first row (a vocabulary slab's first column)
   const float* lse;
   const float* dlogp;
   const float* dent;
@@ -195,6 +198,7 @@ struct DhArgs {
   const int32_t* count;
   float* P;
   int64_t pstride;  // rows per split
+  int32_t accumulate;  // 0: P = the product; 1: P += the product (later vocabulary slabs)
   int32_t* qctr;    // tile-queue counters (QCTR_INTS), zero at launch
 };
 

@@ -65,7 +65,8 @@ __global__ __launch_bounds__(LAYOUT_THREADS) void k_layout(LayoutArgs a) {
     if (lane == 0) carry_s = c;
   }
   // The tile-queue counters of the GEMM kernels that follow on this stream start at 0.
-  if (blk == 0 && tid < a.nqctr) a.qctr[tid] = 0;
+  if (blk == 0)
+    for (int i = tid; i < a.nqctr; i += LAYOUT_THREADS) a.qctr[i] = 0;
   __syncthreads();
   // One workgroup: every pass; several: this block's one pass.
   const int64_t first = (int64_t)blk * LAYOUT_BLOCK;
@@ -850,7 +851,7 @@ __device__ __forceinline__ void grad_epilogue(f32x16 (&acc)[4][NFB], const GradA
     dlc[ni] = live ? dl * a.c1 : 0.f;
     dec[ni] = live ? de * a.c1 : 0.f;
     ez[ni] = ENT ? lse - a.ent[row] : 0.f;
-    tl[ni] = a.tloc[jj] - vbase;
+    tl[ni] = a.tloc[jj] - a.toff - vbase;
   }
   // Stage the bf16 tile as Gs[token][vocab] in LDS, then write full rows.
   __syncthreads();
@@ -926,13 +927,14 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
 
 // dhidden partials: P[split][j][n] = sum over the split's K range of G[j, k] W[k, n]
 // (K = local vocabulary column; G is zero past the real columns, and weight rows past the
-// last real one are read as that row).
+// last real one are read as that row). With G held one vocabulary slab at a time, each slab
+// after the first adds its product into P (slabs in order, so the sum's order is fixed).
 // Tiles: grouped like the vocabulary x token grids with M = scored-row tiles.
 // Waves of the dhidden tile (4: one per SIMD, 128 x 128 each; 8: two per SIMD, 128 x 64). Both
 // give the same partials; 8 waves measured 3.6% slower here (4.09 against 3.94 ms at T=4096).
 constexpr int DH_WAVES = 4;
 
-template <int NW>
+template <int NW, bool ACC>
 __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_dh(DhArgs a) {
   constexpr int NFB = 16 / NW;
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
@@ -968,11 +970,21 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
 #pragma unroll
     for (int ni = 0; ni < NFB; ++ni) {
       const int n = n0 + wn * 32 * NFB + ni * 32 + (lane & 31);
+      float old[16];
+      if constexpr (ACC) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + wm * 128 + mi * 32 + mfma_row(r, lane);
+          old[r] = j < Ts && n < a.H ? P[(int64_t)j * a.H + n] : 0.f;
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = j0 + wm * 128 + mi * 32 + mfma_row(r, lane);
-        if (j < Ts && n < a.H) P[(int64_t)j * a.H + n] = acc[mi][ni][r];
+        if (j < Ts && n < a.H) P[(int64_t)j * a.H + n] = ACC ? old[r] + acc[mi][ni][r] : acc[mi][ni][r];
       }
+      // One 16-value block at a time: the old values of later blocks are not loaded early.
+      if constexpr (ACC) __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -1483,8 +1495,11 @@ hipError_t launch_grad(const GradArgs& a, hipStream_t s) {
 
 hipError_t launch_dh(const DhArgs& a, hipStream_t s) {
   const int n = a.ntm * a.ntn * a.nsplit;
-  if (n > 0)
-    hipLaunchKernelGGL(k_dh<DH_WAVES>, dim3(workers(n)), dim3(64 * DH_WAVES), 0, s, a);
+  if (n > 0 && a.accumulate) {
+    hipLaunchKernelGGL((k_dh<DH_WAVES, true>), dim3(workers(n)), dim3(64 * DH_WAVES), 0, s, a);
+  } else if (n > 0) {
+    hipLaunchKernelGGL((k_dh<DH_WAVES, false>), dim3(workers(n)), dim3(64 * DH_WAVES), 0, s, a);
+  }
   return hipGetLastError();
 }
 

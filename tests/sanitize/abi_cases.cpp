@@ -105,10 +105,19 @@ static void forward_case(const char* name, const Shape& s, bool bias, bool bias_
   if (ws > 0) expect(name, llp_forward(&r, &o, w, ws - 1, nullptr), LLP_ERR_INVALID_ARGUMENT);
 }
 
-static void backward_case(const char* name, const Shape& s, bool bias, bool dent, bool overwrite) {
+static void backward_case(const char* name, const Shape& s, bool bias, bool dent, bool overwrite,
+                          bool slabs = false) {
   Buf b;
   llp_request r = make_request(b, s, true, bias, true, false);
   if (overwrite) r.flags |= LLP_FLAG_OVERWRITE_GRADS;
+  if (slabs) {
+    // G held one vocabulary slab at a time: a smaller workspace than the default mode's.
+    size_t whole = 0, slab = 0;
+    expect(name, llp_workspace_bytes(&r, LLP_OP_BACKWARD, &whole), LLP_OK);
+    r.flags |= LLP_FLAG_G_SLABS;
+    expect(name, llp_workspace_bytes(&r, LLP_OP_BACKWARD, &slab), LLP_OK);
+    expect(name, slab < whole ? LLP_OK : LLP_ERR_INTERNAL, LLP_OK);
+  }
   llp_bwd_in in;
   in.lse = (const float*)b.get((size_t)s.T * 4, 4);
   in.dlogp = (const float*)b.get((size_t)s.T * 4, 4);
@@ -233,7 +242,7 @@ static void malformed_cases() {
       {"rank >= world", [](llp_request& r) { r.vocab.world = 4; r.vocab.rank = 4; r.vocab.local_size = 256; }, LLP_ERR_INVALID_ARGUMENT},
       {"world too big", [](llp_request& r) { r.vocab.world = 65; }, LLP_ERR_INVALID_ARGUMENT},
       {"bad bias dtype", [](llp_request& r) { r.proj.bias = r.proj.weight; r.proj.bias_dtype = 7; }, LLP_ERR_INVALID_ARGUMENT},
-      {"unknown flag", [](llp_request& r) { r.flags = 4; }, LLP_ERR_INVALID_ARGUMENT},
+      {"unknown flag", [](llp_request& r) { r.flags = 8; }, LLP_ERR_INVALID_ARGUMENT},
       {"T too large", [](llp_request& r) { r.layout.num_tokens = int64_t(1) << 23; }, LLP_ERR_UNSUPPORTED},
       {"hidden bytes 2^31", [](llp_request& r) { r.layout.num_tokens = int64_t(1) << 22; r.proj.hidden_stride = 256; }, LLP_ERR_UNSUPPORTED},
       {"T * stride overflow", [](llp_request& r) { r.layout.num_tokens = (int64_t(1) << 23) - 256; r.proj.hidden_stride = (int64_t(1) << 23) - 8; }, LLP_ERR_UNSUPPORTED},
@@ -298,6 +307,11 @@ int main() {
   backward_case("bwd padding-only shard", {64, 64, 4096, 3000, 3072, 1024, 3, 4}, true, false, true);
   backward_case("bwd empty shard", {64, 64, 4096, 3000, 4096, 0, 4, 5}, false, false, true);
   backward_case("bwd no rows overwrite", {0, 64, 1024, 1000, 0, 1024, 0, 1}, true, false, true);
+  backward_case("bwd slabs", {130, 64, 70144, 70000, 0, 70144, 0, 1}, true, true, true, true);
+  backward_case("bwd slabs accumulate", {257, 64, 70144, 70000, 0, 70144, 0, 1}, true, false,
+                false, true);
+  backward_case("bwd slabs shard", {64, 64, 151936, 151669, 113952, 37984, 3, 4}, true, false,
+                true, true);
   replay_cases();
   merge_cases();
   printf("%d cases, %d failed, %lld launches\n", g_cases, g_fail, (long long)llp_stub_launches());

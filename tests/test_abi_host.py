@@ -68,13 +68,13 @@ def test_ctypes_mirror_matches_header(tmp_path):
 
 def test_header_constants_match():
     src = open(HEADER).read()
-    for name in ("LLP_MAX_REPLAY_IDS", "LLP_MAX_WORLD"):
+    for name in ("LLP_MAX_REPLAY_IDS", "LLP_MAX_WORLD", "LLP_G_SLAB_COLUMNS"):
         assert int(re.search(rf"#define {name} (\d+)", src).group(1)) == getattr(A, name)
     for name in ("LLP_STATUS_TARGET_OUT_OF_RANGE", "LLP_STATUS_TARGET_NOT_FOUND",
                  "LLP_STATUS_REPLAY_ID_INVALID", "LLP_STATUS_LAYOUT_INVALID",
                  "LLP_ERR_UNAVAILABLE", "LLP_ERR_INVALID_ARGUMENT", "LLP_ERR_UNSUPPORTED",
                  "LLP_DTYPE_BF16", "LLP_DTYPE_F32", "LLP_OP_FORWARD", "LLP_OP_BACKWARD",
-                 "LLP_FLAG_WANT_ENTROPY", "LLP_FLAG_OVERWRITE_GRADS"):
+                 "LLP_FLAG_WANT_ENTROPY", "LLP_FLAG_OVERWRITE_GRADS", "LLP_FLAG_G_SLABS"):
         assert int(re.search(rf"\b{name} = (\d+)", src).group(1)) == getattr(A, name), name
 
 
@@ -146,7 +146,7 @@ BAD_FORWARD = [
     ("world too big", lambda r: setattr(r.vocab, "world", 65), A.LLP_ERR_INVALID_ARGUMENT),
     ("bad bias dtype", lambda r: (setattr(r.proj, "bias", FAKE), setattr(r.proj, "bias_dtype", 7)),
      A.LLP_ERR_INVALID_ARGUMENT),
-    ("unknown flag", lambda r: setattr(r, "flags", 4), A.LLP_ERR_INVALID_ARGUMENT),
+    ("unknown flag", lambda r: setattr(r, "flags", 8), A.LLP_ERR_INVALID_ARGUMENT),
     ("T too large", lambda r: setattr(r.layout, "num_tokens", 1 << 23), A.LLP_ERR_UNSUPPORTED),
     ("hidden bytes > 4 GiB", lambda r: (setattr(r.layout, "num_tokens", 1 << 20),
                                         setattr(r.proj, "hidden_stride", 4096)), A.LLP_ERR_UNSUPPORTED),
@@ -335,7 +335,10 @@ def test_backward_overwrite_flag_passes_validation():
     r.flags = A.LLP_FLAG_OVERWRITE_GRADS
     st = call()
     assert st != A.LLP_ERR_INVALID_ARGUMENT or "llp_open" in lib.llp_last_error().decode()
-    r.flags = 4
+    r.flags = A.LLP_FLAG_OVERWRITE_GRADS | A.LLP_FLAG_G_SLABS
+    st = call()
+    assert st != A.LLP_ERR_INVALID_ARGUMENT or "llp_open" in lib.llp_last_error().decode()
+    r.flags = 8
     assert call() == A.LLP_ERR_INVALID_ARGUMENT
     assert b"unknown flags" in lib.llp_last_error()
 
@@ -381,7 +384,7 @@ BAD_LOGITS = [
     ("misaligned base", lambda r: setattr(r, "logits", FAKE + 8)),
     ("f32 stride not 16-byte rows", lambda r: setattr(r, "logits_stride", 1026)),
     ("tau zero", lambda r: setattr(r, "temperature", 0.0)),
-    ("unknown flag", lambda r: setattr(r, "flags", 4)),
+    ("unknown flag", lambda r: setattr(r, "flags", 8)),
     ("targets NULL", lambda r: setattr(r, "target_ids", None)),
     ("real > padded", lambda r: setattr(r.vocab, "real_vocab", 2000)),
     ("T = 2^31 (grid limit)", lambda r: setattr(r.layout, "num_tokens", 1 << 31)),

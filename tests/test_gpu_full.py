@@ -350,6 +350,15 @@ def test_full_vocab_dweight_subset(llp, weight):
     check_grad(host(out["dweight"])[vs], rb["dweight"][vs], f"1024-row dweight ({vs.size} rows)")
     assert np.all(host(out["dweight"])[VR:] == 0)
     check_grad(oracle.bf16_to_f64(host(out["dhidden"])), rb["dhidden"], "1024-row dhidden")
+    # G held one vocabulary slab at a time (5 slabs): dweight bitwise the same, dhidden summed
+    # slab by slab.
+    sl = llp.backward(dev_bf16(hb), W, dev(tg), dev(ref["lse"], torch.float32),
+                      dev(dlogp, torch.float32), temperature=TAU, loss_mask=dev(mask),
+                      real_vocab=VR, padded_vocab=VP, g_slabs=True)
+    torch.cuda.synchronize()
+    assert bytes_equal(sl["dweight"], out["dweight"])
+    check_grad(oracle.bf16_to_f64(host(sl["dhidden"])), rb["dhidden"],
+               "1024-row dhidden, G in slabs")
 
 
 # ----------------------------------------------------------------------------- config 5

@@ -524,6 +524,66 @@ def test_backward_overwrite_mode(llp):
     assert all_zero(sw, sb, out["dhidden"])
 
 
+def test_backward_g_slabs(llp):
+    """LLP_FLAG_G_SLABS: G held one vocabulary slab of 32768 columns at a time. 70144 columns
+    make three slabs (the last one ragged, with the padded columns). dweight and dbias are
+    bitwise those of the default mode (each tile's arithmetic is the same); dhidden, summed
+    slab by slab, matches the oracle, repeats bitwise and keeps each row's bits under a
+    permutation of the rows; accumulation into an existing dweight and two vocabulary shards
+    agree with the default mode."""
+    T, H, Vr, Vp, tau = 300, 256, 70000, 70144, 0.7
+    case = synth.small_case(T, H, Vr, Vp, tau, case_id=85, mask_frac=0.2, with_bias=True,
+                            w_std=0.05)
+    f = oracle.forward(case["hidden"], case["weight"], case["bias"], tau, case["targets"],
+                       case["mask"], Vr)
+    g = synth.rng(85, 7)
+    dlogp = g.standard_normal(T) * case["mask"]
+    dent = g.standard_normal(T) * case["mask"]
+    ref = oracle.backward(case["hidden"], case["weight"], case["bias"], tau, case["targets"],
+                          case["mask"], 0, Vp, Vr, f["lse"], dlogp, dent, f["entropy"])
+    args = (llp, case, f["lse"], dlogp, dent, f["entropy"], torch.float32)
+    base = run_backward(*args, overwrite=True)
+    sl = run_backward(*args, overwrite=True, g_slabs=True)
+    assert bytes_equal(sl["dweight"], base["dweight"]) and bytes_equal(sl["dbias"], base["dbias"])
+    dH = oracle.bf16_to_f64(host(sl["dhidden"]))
+    r1 = normwise_rel(dH, ref["dhidden"])
+    say(f"  G in slabs: rel dH {r1:.2e}")
+    assert r1 <= GRAD_RTOL
+    assert np.all(dH[case["mask"] == 0] == 0)
+    again = run_backward(*args, overwrite=True, g_slabs=True)
+    assert bytes_equal(again["dhidden"], sl["dhidden"])
+    perm = synth.rng(85, 8).permutation(T)
+    c2 = dict(case, hidden=case["hidden"][perm], targets=case["targets"][perm],
+              mask=case["mask"][perm])
+    p = run_backward(llp, c2, f["lse"][perm], dlogp[perm], dent[perm], f["entropy"][perm],
+                     torch.float32, overwrite=True, g_slabs=True)
+    np.testing.assert_array_equal(host(sl["dhidden"])[perm], host(p["dhidden"]))
+    # Accumulating into an existing dweight: bitwise the default mode's accumulation.
+    start = torch.randn((Vp, H), device="cuda")
+    acc_base = run_backward(*args, dweight=start.clone())
+    acc_sl = run_backward(*args, dweight=start.clone(), g_slabs=True)
+    assert bytes_equal(acc_sl["dweight"], acc_base["dweight"])
+    # Two shards of 137 tiles (two slabs each; the second holds the real/padded boundary).
+    hid, tg, mk = dev_bf16(case["hidden"]), dev(case["targets"]), dev(case["mask"])
+    W, bias = dev_bf16(case["weight"]), dev_bf16(case["bias"]).float()
+    dH2 = np.zeros((T, H))
+    for r, (lo, hi) in enumerate(((0, 35072), (35072, Vp))):
+        kw = dict(temperature=tau, bias=bias[lo:hi], loss_mask=mk, offset=lo, real_vocab=Vr,
+                  padded_vocab=Vp, rank=r, world=2, dentropy=dev(dent, torch.float32),
+                  entropy=dev(f["entropy"], torch.float32), overwrite=True)
+        a = llp.backward(hid, W[lo:hi], tg, dev(f["lse"], torch.float32),
+                         dev(dlogp, torch.float32), **kw)
+        b = llp.backward(hid, W[lo:hi], tg, dev(f["lse"], torch.float32),
+                         dev(dlogp, torch.float32), g_slabs=True, **kw)
+        torch.cuda.synchronize()
+        assert bytes_equal(a["dweight"], b["dweight"]) and bytes_equal(a["dbias"], b["dbias"])
+        assert bytes_equal(b["dweight"], base["dweight"][lo:hi])
+        dH2 += oracle.bf16_to_f64(host(b["dhidden"]))
+    r2 = normwise_rel(dH2, ref["dhidden"])
+    say(f"  two shards, G in slabs: rel summed dH {r2:.2e}")
+    assert r2 <= GRAD_RTOL
+
+
 def test_forward_batch_size_invariance_bitwise(llp):
     """The same rows in batches of different size get the same bits: 5700 rows over 12
     vocabulary tiles make 276 tiles (more than one round on a 256-CU device); 700 of those rows
