@@ -404,7 +404,7 @@ def measure_config4(llp, W, stream, busy, reps=2):
     lse = torch.empty(Tp, dtype=torch.float32, device="cuda")
     ws = {}
 
-    def one_pass_whole():
+    def one_pass_whole(slabs=False):
         # The forward in chunks of 4096 rows as above; then ONE backward over the whole pack
         # with the chunks' lse: dweight is written once (no read-modify-write per chunk).
         for c0, c1 in chunks:
@@ -413,7 +413,7 @@ def measure_config4(llp, W, stream, busy, reps=2):
             lse[c0:c1] = o["lse"]
         llp.backward(h, W, tg, lse, dl, temperature=TAU, loss_mask=mk, real_vocab=VR,
                      padded_vocab=VP, dweight=dW, dhidden=dH, overwrite=True,
-                     workspace=ws.get("bwd"))
+                     workspace=ws.get("bwd_slabs" if slabs else "bwd"), g_slabs=slabs)
 
     def timed(fn):
         fn()
@@ -435,8 +435,15 @@ def measure_config4(llp, W, stream, busy, reps=2):
     ws["bwd"] = torch.empty(llp.workspace_bytes(req, capi.LLP_OP_BACKWARD), dtype=torch.uint8,
                             device="cuda")
     ms_whole = timed(one_pass_whole)
-    flop = 4.0 * 2.0 * H * VR * scored   # forward + the backward's three products
     ws_gb = ws["bwd"].numel() / 1e9
+    del ws["bwd"]
+    # The same whole-pack backward with G held one vocabulary slab at a time.
+    req.flags |= capi.LLP_FLAG_G_SLABS
+    ws["bwd_slabs"] = torch.empty(llp.workspace_bytes(req, capi.LLP_OP_BACKWARD),
+                                  dtype=torch.uint8, device="cuda")
+    ms_slabs = timed(lambda: one_pass_whole(True))
+    ws_slab_gb = ws["bwd_slabs"].numel() / 1e9
+    flop = 4.0 * 2.0 * H * VR * scored   # forward + the backward's three products
     del h, tg, mk, dl, dH, dW, lse, ws
     torch.cuda.empty_cache()
     return {"config4_forward_backward": {
@@ -450,7 +457,12 @@ def measure_config4(llp, W, stream, busy, reps=2):
             "tflops": flop / (ms_whole * 1e-3) / 1e12, "backward_workspace_GB": ws_gb,
             "workload": "the same pass: forward per 4096-row chunk, then one backward over "
                         "all 56583 rows (dweight written once; logp and dhidden rows bitwise "
-                        "those of the chunked pass, dweight equal to rounding)"}}
+                        "those of the chunked pass, dweight equal to rounding)"},
+        "config4_forward_chunked_backward_whole_g_slabs": {
+            "ms": ms_slabs, "scored_tokens_per_s": scored / (ms_slabs * 1e-3),
+            "tflops": flop / (ms_slabs * 1e-3) / 1e12, "backward_workspace_GB": ws_slab_gb,
+            "workload": "the whole-pack pass above with LLP_FLAG_G_SLABS: G held one slab of "
+                        "32768 vocabulary columns at a time"}}
 
 
 def main():
@@ -461,8 +473,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2560)
     ap.add_argument("--skip-config4", action="store_true",
-                    help="leave out the config-4 measurement (profiling runs: its chunks would "
-                         "mix other forward/backward shapes into the per-kernel averages)")
+                    help="leave out the config-4 and slab-mode backward measurements (profiling "
+                         "runs: their launches would mix other shapes into the per-kernel "
+                         "averages)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy before the warm-up (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -589,10 +602,37 @@ def main():
     ea[1].record(stream)
     torch.cuda.synchronize()
     bwd_bias_ms = float(ea[0].elapsed_time(ea[1])) / 5
+    # The backward with G held one vocabulary slab at a time (LLP_FLAG_G_SLABS): the same rows,
+    # dweight overwritten, 1 + 5 calls; its workspace beside the default mode's.
+    import lm_head_linear_logp_amd._capi as capi
+
+    def bwd_ws(slabs):
+        r = llp._request(h, W, tg, TAU, None, None, None, 0, VR, VP, 0, 1, False, None)
+        r.flags |= capi.LLP_FLAG_OVERWRITE_GRADS | (capi.LLP_FLAG_G_SLABS if slabs else 0)
+        return llp.workspace_bytes(r, capi.LLP_OP_BACKWARD)
+    bwd_slab_ms = ws_slab_gb = None
+    ws_default_gb = bwd_ws(False) / 1e9
+    if not args.skip_config4:
+        ws_slab = torch.empty(bwd_ws(True), dtype=torch.uint8, device="cuda")
+
+        def bwd_slabs():
+            llp.backward(h, W, tg, mg["lse"], dlogp, temperature=TAU, real_vocab=VR,
+                         padded_vocab=VP, dweight=dW, dhidden=dH, overwrite=True, g_slabs=True,
+                         workspace=ws_slab)
+        bwd_slabs()
+        ea[0].record(stream)
+        for _ in range(5):
+            bwd_slabs()
+        ea[1].record(stream)
+        torch.cuda.synchronize()
+        bwd_slab_ms = float(ea[0].elapsed_time(ea[1])) / 5
+        ws_slab_gb = ws_slab.numel() / 1e9
+        del ws_slab
     del mg, mgb, bias, dbias
     log(f"phases (ms): forward {fwd_ms:.3f} merge {merge_ms:.3f} backward {bwd_ms:.3f} "
         f"top-p {topp_ms:.3f}; step {ms_per_step:.3f} (host wall {1e3 * wall / args.steps:.3f}); "
-        f"backward with dweight accumulated {bwd_acc_ms:.3f}, with a bias {bwd_bias_ms:.3f}")
+        f"backward with dweight accumulated {bwd_acc_ms:.3f}, with a bias {bwd_bias_ms:.3f}, "
+        f"G in slabs {bwd_slab_ms}")
 
     flop_fwd = 2.0 * T * H * VR
     ach_fwd = flop_fwd / (fwd_ms * 1e-3) / 1e12
@@ -639,6 +679,12 @@ def main():
                                "what": "llp_backward of the same rows with an fp32 bias "
                                        "[151936] and its gradient, dweight and dbias "
                                        "overwritten, 5 calls after the timed steps"},
+        "backward_g_slabs": {"ms": bwd_slab_ms,
+                             "tflops": flop_bwd / (bwd_slab_ms * 1e-3) / 1e12 if bwd_slab_ms else None,
+                             "workspace_GB": ws_slab_gb, "default_workspace_GB": ws_default_gb,
+                             "what": "llp_backward with LLP_FLAG_G_SLABS (G held one slab of "
+                                     "32768 vocabulary columns at a time, 5 slabs), dweight "
+                                     "overwritten, 5 calls after the timed steps"},
         "forward_backward_tflops": (flop_fwd + flop_bwd) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12,
         "top_p": {"us": topp_ms * 1e3, "algorithmic_bytes": topp_bytes,
                   "GBps": topp_bytes / (topp_ms * 1e-3) / 1e9, "peak_GBps": PEAK_HBM_GBS},

@@ -935,7 +935,7 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
 constexpr int DH_WAVES = 4;
 
 template <int NW, bool ACC>
-__global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_dh(DhArgs a) {
+__device__ __forceinline__ void dh_tile(const DhArgs& a) {
   constexpr int NFB = 16 / NW;
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma::LDS_BYTES / 2];
   const int per = a.ntm * a.ntn;
@@ -989,6 +989,17 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
 }
 
 // dhidden[row] = bf16(sum over splits in order); unscored rows are zero.
+// The dhidden product (first vocabulary slab, or the only one) and the same product added into
+// the partials of the slabs before it.
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_dh(DhArgs a) {
+  dh_tile<NW, false>(a);
+}
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_dh_acc(DhArgs a) {
+  dh_tile<NW, true>(a);
+}
+
 __global__ __launch_bounds__(256) void k_dh_reduce(DhReduceArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t cpr = a.H / 8;  // 8-column chunks per row
@@ -1496,9 +1507,9 @@ hipError_t launch_grad(const GradArgs& a, hipStream_t s) {
 hipError_t launch_dh(const DhArgs& a, hipStream_t s) {
   const int n = a.ntm * a.ntn * a.nsplit;
   if (n > 0 && a.accumulate) {
-    hipLaunchKernelGGL((k_dh<DH_WAVES, true>), dim3(workers(n)), dim3(64 * DH_WAVES), 0, s, a);
+    hipLaunchKernelGGL(k_dh_acc<DH_WAVES>, dim3(workers(n)), dim3(64 * DH_WAVES), 0, s, a);
   } else if (n > 0) {
-    hipLaunchKernelGGL((k_dh<DH_WAVES, false>), dim3(workers(n)), dim3(64 * DH_WAVES), 0, s, a);
+    hipLaunchKernelGGL(k_dh<DH_WAVES>, dim3(workers(n)), dim3(64 * DH_WAVES), 0, s, a);
   }
   return hipGetLastError();
 }
