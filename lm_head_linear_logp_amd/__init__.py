@@ -521,13 +521,13 @@ class _LinearLogp(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, hidden, weight, bias, target_ids, loss_mask, temperature, real_vocab,
-                padded_vocab, want_entropy):
+                padded_vocab, want_entropy, g_slabs):
         out = forward(hidden, weight, target_ids, temperature=temperature, bias=bias,
                       loss_mask=loss_mask, real_vocab=real_vocab, padded_vocab=padded_vocab,
                       want_entropy=want_entropy)
         ctx.save_for_backward(hidden, weight, bias, target_ids, loss_mask, out["lse"],
                               out["entropy"])
-        ctx.cfg = (temperature, real_vocab, padded_vocab)
+        ctx.cfg = (temperature, real_vocab, padded_vocab, g_slabs)
         ctx.mark_non_differentiable(out["lse"])
         ent = out["entropy"] if want_entropy else out["lse"].new_zeros(0)
         return out["logp"], ent, out["lse"]
@@ -535,7 +535,7 @@ class _LinearLogp(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dlogp, dentropy, _dlse):
         hidden, weight, bias, target_ids, loss_mask, lse, entropy = ctx.saved_tensors
-        temperature, real_vocab, padded_vocab = ctx.cfg
+        temperature, real_vocab, padded_vocab, g_slabs = ctx.cfg
         T = hidden.shape[0]
         if dlogp is None:
             dlogp = torch.zeros(T, dtype=torch.float32, device=hidden.device)
@@ -545,17 +545,18 @@ class _LinearLogp(torch.autograd.Function):
                      real_vocab=real_vocab, padded_vocab=padded_vocab,
                      dentropy=dentropy.float().contiguous() if use_ent else None,
                      entropy=entropy if use_ent else None, overwrite=True,
-                     want_dbias=bias is not None and ctx.needs_input_grad[2])
+                     want_dbias=bias is not None and ctx.needs_input_grad[2], g_slabs=g_slabs)
         dW = g["dweight"].to(weight.dtype) if ctx.needs_input_grad[1] else None
         db = g["dbias"].to(bias.dtype) if bias is not None and ctx.needs_input_grad[2] else None
         dH = g["dhidden"] if ctx.needs_input_grad[0] else None
-        return dH, dW, db, None, None, None, None, None, None
+        return dH, dW, db, None, None, None, None, None, None, None
 
 
 def linear_logp(hidden: torch.Tensor, weight: torch.Tensor, target_ids: torch.Tensor, *,
                 temperature: float, bias: Optional[torch.Tensor] = None,
                 loss_mask: Optional[torch.Tensor] = None, real_vocab: Optional[int] = None,
-                padded_vocab: Optional[int] = None, want_entropy: bool = True):
+                padded_vocab: Optional[int] = None, want_entropy: bool = True,
+                g_slabs: bool = False):
     """Per-token log-probability of target_ids (and entropy) under softmax((h W^T + b) / tau)
     over the real vocabulary, differentiable in hidden, weight and bias: the operator's
     forward, and in autograd's backward pass its backward with the incoming dlogp/dentropy
@@ -563,8 +564,9 @@ def linear_logp(hidden: torch.Tensor, weight: torch.Tensor, target_ids: torch.Te
     Returns (logp, entropy, lse); entropy is an empty tensor when want_entropy is False, and
     lse carries no gradient. Rows with loss_mask 0 give logp = entropy = 0 and no gradient.
     The weight and bias gradients are computed in fp32 and handed to autograd in the
-    parameters' dtype."""
+    parameters' dtype. g_slabs: the backward holds G one vocabulary slab at a time
+    (LLP_FLAG_G_SLABS)."""
     if loss_mask is not None and loss_mask.dtype == torch.bool:
         loss_mask = loss_mask.to(torch.uint8)
     return _LinearLogp.apply(hidden, weight, bias, target_ids, loss_mask, temperature,
-                             real_vocab, padded_vocab, want_entropy)
+                             real_vocab, padded_vocab, want_entropy, g_slabs)

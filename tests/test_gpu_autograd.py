@@ -77,3 +77,26 @@ def test_autograd_without_entropy_output(llp):
     assert bytes_equal(logp, ref["logp"])
     assert bytes_equal(h.grad, gr["dhidden"])
     assert bytes_equal(W.grad, gr["dweight"].to(torch.bfloat16))
+
+
+def test_autograd_with_g_slabs(llp):
+    # 157 vocabulary tiles: two slabs of G in the backward.
+    T, H, Vr, Vp, tau = 64, 128, 40000, 40192, 0.7
+    c = synth.small_case(T, H, Vr, Vp, tau, case_id=87, w_std=0.05)
+    h = dev_bf16(c["hidden"]).requires_grad_(True)
+    W = dev_bf16(c["weight"]).requires_grad_(True)
+    tg = dev(c["targets"])
+    logp, ent, _ = llp.linear_logp(h, W, tg, temperature=tau, real_vocab=Vr, padded_vocab=Vp,
+                                   g_slabs=True)
+    (logp.sum() + 0.5 * ent.sum()).backward()
+    torch.cuda.synchronize()
+    with torch.no_grad():
+        ref = llp.forward(h.detach(), W.detach(), tg, temperature=tau, real_vocab=Vr,
+                          padded_vocab=Vp)
+        gr = llp.backward(h.detach(), W.detach(), tg, ref["lse"], torch.ones(T, device="cuda"),
+                          temperature=tau, real_vocab=Vr, padded_vocab=Vp,
+                          dentropy=torch.full((T,), 0.5, device="cuda"), entropy=ref["entropy"],
+                          overwrite=True, g_slabs=True)
+        torch.cuda.synchronize()
+    assert bytes_equal(h.grad, gr["dhidden"])
+    assert bytes_equal(W.grad, gr["dweight"].to(torch.bfloat16))
