@@ -323,8 +323,9 @@ typedef struct {
 LLP_API llp_status llp_open(int32_t device, llp_info* info);
 
 /* Workspace bytes an execution call needs for `req` and `op` (LLP_OP_FORWARD or
- * LLP_OP_BACKWARD): a pure function of the shapes. The caller allocates it (device memory,
- * 256-byte aligned) and passes it to that call. */
+ * LLP_OP_BACKWARD): a pure function of the shapes (and, for the backward, of
+ * LLP_FLAG_G_SLABS). The caller allocates it (device memory, 256-byte aligned) and passes it
+ * to that call. */
 LLP_API llp_status llp_workspace_bytes(const llp_request* req, int32_t op, size_t* bytes);
 
 /* Fused forward for one shard: per row, z over the shard's real columns, lse, the target
