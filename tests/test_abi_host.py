@@ -245,6 +245,29 @@ def test_workspace_bytes_pure_function():
     assert lib.llp_workspace_bytes(C.byref(r), 3, C.byref(nb)) == A.LLP_ERR_INVALID_ARGUMENT
 
 
+def test_slab_flag_sizes_g_for_one_slab():
+    """LLP_FLAG_G_SLABS: the backward workspace holds G for one slab of LLP_G_SLAB_COLUMNS
+    columns; the forward's workspace does not depend on it, nor does a shard of one slab."""
+    lib = A.load()
+
+    def ws(r, op):
+        n = C.c_size_t()
+        assert lib.llp_workspace_bytes(C.byref(r), op, C.byref(n)) == A.LLP_OK
+        return n.value
+    r = good_request()
+    full_b, full_f = ws(r, A.LLP_OP_BACKWARD), ws(r, A.LLP_OP_FORWARD)
+    r.flags = A.LLP_FLAG_G_SLABS
+    slab_b = ws(r, A.LLP_OP_BACKWARD)
+    assert ws(r, A.LLP_OP_FORWARD) == full_f
+    g_full, g_slab = 4096 * 594 * 256 * 2, 4096 * A.LLP_G_SLAB_COLUMNS * 2
+    assert full_b - slab_b >= g_full - g_slab - (1 << 16)
+    assert slab_b < full_b / 3
+    small = good_request(V=A.LLP_G_SLAB_COLUMNS, Vr=A.LLP_G_SLAB_COLUMNS - 5)
+    a = ws(small, A.LLP_OP_BACKWARD)
+    small.flags = A.LLP_FLAG_G_SLABS
+    assert ws(small, A.LLP_OP_BACKWARD) == a
+
+
 def _merge(world, parts, T=16, out=None):
     lib = A.load()
     arr = (A.llp_partials * max(world, 1))(*parts) if parts else None
