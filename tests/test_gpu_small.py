@@ -584,6 +584,23 @@ def test_backward_g_slabs(llp):
     assert r2 <= GRAD_RTOL
 
 
+def test_backward_g_slabs_bf16_bias_odd_k_steps(llp):
+    # H = 320 (5 K steps), a bf16 bias, 258 vocabulary tiles: slabs of 128, 128 and 2 tiles.
+    T, H, Vr, Vp, tau = 129, 320, 66000, 66048, 1.3
+    case = synth.small_case(T, H, Vr, Vp, tau, case_id=86, with_bias=True, w_std=0.05)
+    f = oracle.forward(case["hidden"], case["weight"], case["bias"], tau, case["targets"], None,
+                       Vr)
+    dlogp = synth.rng(86, 7).standard_normal(T)
+    ref = oracle.backward(case["hidden"], case["weight"], case["bias"], tau, case["targets"],
+                          None, 0, Vp, Vr, f["lse"], dlogp)
+    base = run_backward(llp, case, f["lse"], dlogp, overwrite=True)
+    sl = run_backward(llp, case, f["lse"], dlogp, overwrite=True, g_slabs=True)
+    assert bytes_equal(sl["dweight"], base["dweight"]) and bytes_equal(sl["dbias"], base["dbias"])
+    r = normwise_rel(oracle.bf16_to_f64(host(sl["dhidden"])), ref["dhidden"])
+    say(f"  G in slabs, H=320, bf16 bias: rel dH {r:.2e}")
+    assert r <= GRAD_RTOL
+
+
 def test_forward_batch_size_invariance_bitwise(llp):
     """The same rows in batches of different size get the same bits: 5700 rows over 12
     vocabulary tiles make 276 tiles (more than one round on a 256-CU device); 700 of those rows
