@@ -1,6 +1,6 @@
 """The execution calls under HIP graph capture ([CUDA provider, "Changes"]: the provider calls
 must be capturable into CUDA/HIP graphs). Forward + backward with caller-allocated outputs and
-workspace, the forward in the library's static scratch, and the replay-side calls (compact
+workspace (G whole, and G in vocabulary slabs), the forward in the library's static scratch, and the replay-side calls (compact
 replay over 4 shards and their merge, the logits-input forward, the dense keep-mask replay;
 their outputs allocated from the graph's pool during capture) are captured once and replayed
 several times. Between replays the program does its own eager work, overwrites the graph's
@@ -50,10 +50,11 @@ def _buffers(llp, x):
     return fo, req, fws, bws, go
 
 
-def _step(llp, x, fo, req, fws, bws, go):
+def _step(llp, x, fo, req, fws, bws, go, g_slabs=False):
     llp.forward(x["h"], x["W"], x["tg"], workspace=fws, out=fo, **req)
     llp.backward(x["h"], x["W"], x["tg"], fo["lse"], x["dl"], overwrite=True, workspace=bws,
-                 dhidden=go["dhidden"], dweight=go["dweight"], dbias=go["dbias"], **req)
+                 dhidden=go["dhidden"], dweight=go["dweight"], dbias=go["dbias"],
+                 g_slabs=g_slabs, **req)
 
 
 def _snapshot(fo, go):
@@ -68,30 +69,32 @@ def _poison(fo, go):
             t.fill_(float("nan"))
 
 
-def test_forward_backward_replays_match_eager(llp):
+@pytest.mark.parametrize("g_slabs", [False, True], ids=["g_whole", "g_slabs"])
+def test_forward_backward_replays_match_eager(llp, g_slabs):
+    # With g_slabs the backward runs its kernels once per vocabulary slab (three here).
     x = _case()
     fo, req, fws, bws, go = _buffers(llp, x)
-    say(f"graph: eager forward + backward T={T} H={H} V={VR}/{VP}")
-    _step(llp, x, fo, req, fws, bws, go)
+    say(f"graph: eager forward + backward T={T} H={H} V={VR}/{VP} g_slabs={g_slabs}")
+    _step(llp, x, fo, req, fws, bws, go, g_slabs)
     torch.cuda.synchronize()
     ref = _snapshot(fo, go)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        _step(llp, x, fo, req, fws, bws, go)
+        _step(llp, x, fo, req, fws, bws, go, g_slabs)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     say("graph: capture")
     with torch.cuda.graph(g):
-        _step(llp, x, fo, req, fws, bws, go)
+        _step(llp, x, fo, req, fws, bws, go, g_slabs)
     torch.cuda.synchronize()
     other = _case()
     other["dl"] = other["dl"] * 2
     ob = _buffers(llp, other)
     for rep in range(4):
         say(f"graph: replay {rep}")
-        _step(llp, other, *ob)          # the program's own eager work between replays
+        _step(llp, other, *ob, g_slabs)          # the program's own eager work between replays
         _poison(fo, go)
         torch.cuda.synchronize()
         g.replay()
